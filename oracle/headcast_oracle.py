@@ -1,0 +1,497 @@
+"""Plain fp64 CPU oracle for HeadCast head-routed attention.
+
+TEST INFRASTRUCTURE ONLY.  Only the test-suite, the smoke check and the
+benchmark's CPU-baseline leg may import this module.  The GPU product path
+never calls it and shares no code, table or helper with it.
+
+Sources (cited by page and section; the pages print no equations, so every
+formula below is the plainest reading of their prose, restated here):
+
+  [Pith]  pith.science review page "HeadCast: Casting Attention Heads for
+          Efficient Autoregressive Video Generation" (arXiv 2607.20125):
+          sections "The pith", "Core claim", "What carries the argument",
+          "Referee Report" (major comments 2 and 3 cite the paper's
+          Sec. 4.2 Eq. 3-5, Sec. 4.4, Sec. 5.1, Sec. 5.5), "Axiom &
+          Free-Parameter Ledger", and the captions of Fig. 1, 3, 7 and 8.
+  [Abs]   the paper's abstract (codewithpapers.app record of arXiv 2607.20125).
+
+What is computed
+  * Four archetypes.  Sink heads read only the first cached block, Dummy heads
+    only the newest block, Spatial heads a fixed latent-grid cell in every
+    cached frame, Global heads the whole sliding window ([Pith] "The pith",
+    "Core claim", Fig. 1 / Fig. 7 / Fig. 8 captions).
+  * Every pathway is EXACT softmax attention over a per-query key set; the
+    method saves work only by shrinking that set.  So the oracle is the
+    textbook definition: masked softmax attention, in fp64.
+  * Spatial cells: each frame is cut into non-overlapping 10x10 cells
+    ([Pith] ledger "deployed spatial grid cell", Fig. 3 caption, Referee
+    comment 2 on Sec. 4.4).  Reading adopted for "with rounded remainder":
+    cells anchored at (0, 0), ceil(g/10) per axis, the last row / column of
+    cells truncated at the frame edge.
+  * Classifier ([Pith] "What carries the argument", ledger, Referee comments
+    2-3 on Sec. 4.2 Eq. 2-5): per head, the full-context output is compared
+    with the Sink, Dummy and Spatial proxy outputs by cosine similarity;
+    thresholds 0.95; Spatial is additionally gated by a worst-case score,
+    5th percentile of the per-query cosines minus gamma * MSE (gamma = 5,
+    threshold 0.755); a head that clears no proxy is Global.
+    Readings adopted where the pages are silent: per-query cosines averaged
+    over queries; percentile = linear interpolation between order statistics
+    at position p/100*(n-1); MSE = mean over all query rows and channels of
+    the squared difference between full and Spatial outputs; rule 0 picks the
+    cleared proxy with the largest mean cosine (ties Sink < Dummy < Spatial),
+    rule 1 the first cleared proxy in the order Sink, Dummy, Spatial.
+  * Cache restructure ([Pith] "What carries the argument"; [Abs]): the
+    monolithic cache is split per head: Sink and Dummy keep one block, Global
+    the full sliding window, Spatial the full window stored cell by cell.
+
+Pins: every function here is checked by the `not gpu` tests against closed
+forms, invariants, library routines (torch SDPA in float64, numpy.percentile)
+and brute force on tiny inputs.  No function is "parity unpinned".
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+
+SINK, DUMMY, SPATIAL, GLOBAL = 0, 1, 2, 3
+LABEL_NAMES = ("sink", "dummy", "spatial", "global")
+# Classification-only variant of the Spatial proxy: the (2r+1)x(2r+1) sliding
+# neighbourhood the review says the paper classifies with ([Pith] Referee
+# comment 2, ledger "Spatial proxy radius r = 2").
+SLIDING = 4
+
+QUERY_CHUNK = 512  # rows per fp64 chunk; rows are independent, this only bounds memory
+
+
+@dataclass(frozen=True)
+class Geometry:
+    """Latent video geometry of one attention layer.
+
+    Tokens are frame-major then row-major: t = f*T + y*grid_w + x.  The window
+    holds `window_frames` frames, oldest first; the queries are the newest
+    block (its `block_frames` frames are the last ones of the window)."""
+    grid_h: int
+    grid_w: int
+    block_frames: int
+    window_frames: int
+    cell_h: int = 10
+    cell_w: int = 10
+
+    @property
+    def T(self) -> int:
+        return self.grid_h * self.grid_w
+
+    @property
+    def Nq(self) -> int:
+        return self.block_frames * self.T
+
+    @property
+    def Nk(self) -> int:
+        return self.window_frames * self.T
+
+    @property
+    def cell_rows(self) -> int:
+        return -(-self.grid_h // self.cell_h)
+
+    @property
+    def cell_cols(self) -> int:
+        return -(-self.grid_w // self.cell_w)
+
+    @property
+    def n_cells(self) -> int:
+        return self.cell_rows * self.cell_cols
+
+    def split_token(self, t):
+        """token index -> (frame, y, x)."""
+        t = np.asarray(t)
+        return t // self.T, (t % self.T) // self.grid_w, t % self.grid_w
+
+    def cell_of(self, y, x):
+        return (np.asarray(y) // self.cell_h) * self.cell_cols + np.asarray(x) // self.cell_w
+
+    def cell_box(self, c):
+        """cell id -> (y0, y1, x0, x1), half-open, truncated at the frame edge."""
+        cy, cx = divmod(int(c), self.cell_cols)
+        y0, x0 = cy * self.cell_h, cx * self.cell_w
+        return y0, min(y0 + self.cell_h, self.grid_h), x0, min(x0 + self.cell_w, self.grid_w)
+
+    def cell_size(self, c) -> int:
+        y0, y1, x0, x1 = self.cell_box(c)
+        return (y1 - y0) * (x1 - x0)
+
+
+def default_scale(d: int) -> float:
+    """Softmax temperature of standard scaled dot-product attention, 1/sqrt(d)."""
+    return 1.0 / math.sqrt(d)
+
+
+# ----------------------------------------------------------------------------
+# Key sets: two independent formulations (a boolean mask over the window, and
+# an explicit per-query key list), so each checks the other.
+# ----------------------------------------------------------------------------
+def key_mask(geom: Geometry, pathway: int, n_frames: int | None = None, radius: int = 2):
+    """Boolean [Nq, n_frames*T]: may query i attend to window key j?
+
+    Queries are the last block of the window: query i sits in window frame
+    n_frames - B + i // T at the same (y, x) split as a key."""
+    nf = geom.window_frames if n_frames is None else n_frames
+    B, T = geom.block_frames, geom.T
+    qi = np.arange(B * T)
+    kj = np.arange(nf * T)
+    _, qy, qx = geom.split_token(qi)
+    kf, ky, kx = geom.split_token(kj)
+    if pathway == GLOBAL:
+        return np.ones((qi.size, kj.size), dtype=bool)
+    if pathway == SINK:       # first block of the window
+        return np.broadcast_to(kf < B, (qi.size, kj.size)).copy()
+    if pathway == DUMMY:      # newest block = the queries' own block
+        return np.broadcast_to(kf >= nf - B, (qi.size, kj.size)).copy()
+    if pathway == SPATIAL:    # same grid cell, any frame
+        return geom.cell_of(qy, qx)[:, None] == geom.cell_of(ky, kx)[None, :]
+    if pathway == SLIDING:    # (2r+1)^2 box around the query, any frame, cut at borders
+        return (np.abs(qy[:, None] - ky[None, :]) <= radius) & (np.abs(qx[:, None] - kx[None, :]) <= radius)
+    raise ValueError(f"unknown pathway {pathway}")
+
+
+def key_list(geom: Geometry, pathway: int, i: int, n_frames: int | None = None, radius: int = 2):
+    """Window key indices query i attends to, enumerated frame by frame."""
+    nf = geom.window_frames if n_frames is None else n_frames
+    B, T, gw, gh = geom.block_frames, geom.T, geom.grid_w, geom.grid_h
+    y, x = (i % T) // gw, i % gw
+    if pathway == GLOBAL:
+        return np.arange(nf * T)
+    if pathway == SINK:
+        return np.arange(B * T)
+    if pathway == DUMMY:
+        return np.arange((nf - B) * T, nf * T)
+    if pathway == SPATIAL:
+        y0 = (y // geom.cell_h) * geom.cell_h
+        x0 = (x // geom.cell_w) * geom.cell_w
+        ys = range(y0, min(y0 + geom.cell_h, gh))
+        xs = range(x0, min(x0 + geom.cell_w, gw))
+    elif pathway == SLIDING:
+        ys = range(max(0, y - radius), min(gh, y + radius + 1))
+        xs = range(max(0, x - radius), min(gw, x + radius + 1))
+    else:
+        raise ValueError(f"unknown pathway {pathway}")
+    return np.array([f * T + yy * gw + xx for f in range(nf) for yy in ys for xx in xs], dtype=np.int64)
+
+
+# ----------------------------------------------------------------------------
+# Attention (definition): o_i = sum_j softmax_j(s <q_i, k_j>) v_j over the key set.
+# ----------------------------------------------------------------------------
+def attention_masked(q, k, v, mask, scale: float, rows=None):
+    """fp64 masked softmax attention for one head.
+
+    q [Nq, d], k [Nk, d], v [Nk, dv], mask [Nq, Nk] bool.  Returns [len(rows), dv].
+    Each row must have at least one allowed key."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    rows = np.arange(q.shape[0]) if rows is None else np.asarray(rows)
+    out = np.empty((rows.size, v.shape[1]), dtype=np.float64)
+    for s in range(0, rows.size, QUERY_CHUNK):
+        r = rows[s:s + QUERY_CHUNK]
+        logits = scale * (q[r] @ k.T)
+        m = mask[r]
+        logits = np.where(m, logits, -np.inf)
+        mx = logits.max(axis=1, keepdims=True)
+        p = np.exp(logits - mx)           # exp(-inf) = 0 for masked keys
+        p /= p.sum(axis=1, keepdims=True)
+        out[s:s + r.size] = p @ v
+    return out
+
+
+def attention_keylist(q, k, v, keylists, scale: float):
+    """fp64 attention, one query at a time over an explicit key list."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    out = np.empty((len(keylists), v.shape[1]), dtype=np.float64)
+    for n, (qi, keys) in enumerate(keylists):
+        lg = scale * (k[keys] @ q[qi])
+        w = np.exp(lg - lg.max())
+        out[n] = (w / w.sum()) @ v[keys]
+    return out
+
+
+def attend_head(q, k, v, pathway: int, geom: Geometry, scale: float | None = None,
+                rows=None, n_frames: int | None = None, radius: int = 2):
+    """One head's output for one pathway over a frame-major window k/v."""
+    scale = default_scale(q.shape[1]) if scale is None else scale
+    nf = k.shape[0] // geom.T if n_frames is None else n_frames
+    mask = key_mask(geom, pathway, nf, radius)
+    return attention_masked(q, k, v, mask, scale, rows)
+
+
+def routed_attention(q, k_win, v_win, labels, geom: Geometry, scale: float | None = None,
+                     rows=None, k_sink=None, v_sink=None):
+    """Head-routed attention: every head attends over its archetype's key set.
+
+    q [H, Nq, d]; k_win / v_win [H, nf*T, d] frame-major, oldest frame first,
+    the queries' own block last; labels int [H].  Sink heads read frames
+    [0, B) of the window unless the sink block is given explicitly
+    (k_sink / v_sink [H, B*T, d]), as after the window has slid past the
+    video's first block.  Returns fp64 [H, len(rows) or Nq, d]."""
+    H = q.shape[0]
+    outs = []
+    for h in range(H):
+        lab = int(labels[h])
+        if lab == SINK and k_sink is not None:
+            # whole sink block, no mask
+            m = np.ones((geom.Nq, geom.block_frames * geom.T), dtype=bool)
+            sc = default_scale(q.shape[2]) if scale is None else scale
+            outs.append(attention_masked(q[h], k_sink[h], v_sink[h], m, sc, rows))
+        else:
+            outs.append(attend_head(q[h], k_win[h], v_win[h], lab, geom, scale, rows))
+    return np.stack(outs)
+
+
+# ----------------------------------------------------------------------------
+# Classifier (Eq. 2-5 as read from the review's prose).
+# ----------------------------------------------------------------------------
+@dataclass(frozen=True)
+class ClassifyParams:
+    theta_sink: float = 0.95
+    theta_dummy: float = 0.95
+    theta_spatial: float = 0.95
+    theta_score: float = 0.755
+    gamma: float = 5.0
+    percentile: float = 5.0
+    rule: int = 0            # 0: argmax of cleared proxies, 1: first cleared in order
+    spatial_proxy: int = 0   # 0: deployed grid cell, 1: sliding (2r+1)^2 box
+    radius: int = 2
+
+
+def cosine_rows(a, b):
+    """Per-row cosine similarity; 0 where either row has zero norm."""
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    dot = np.einsum("ij,ij->i", a, b)
+    na = np.sqrt(np.einsum("ij,ij->i", a, a))
+    nb = np.sqrt(np.einsum("ij,ij->i", b, b))
+    den = na * nb
+    return np.where(den > 0, dot / np.where(den > 0, den, 1.0), 0.0)
+
+
+def percentile_linear(x, p: float) -> float:
+    """p-th percentile, linear interpolation between order statistics at
+    fractional rank p/100 * (n-1)."""
+    s = np.sort(np.asarray(x, dtype=np.float64))
+    pos = p / 100.0 * (s.size - 1)
+    lo = int(math.floor(pos))
+    hi = min(lo + 1, s.size - 1)
+    return float(s[lo] + (s[hi] - s[lo]) * (pos - lo))
+
+
+def classifier_outputs(q, k, v, geom: Geometry, scale: float | None = None,
+                       spatial_proxy: int = 0, radius: int = 2):
+    """The four outputs the classifier compares, each [H, Nq, d] fp64:
+    full context, Sink proxy, Dummy proxy, Spatial proxy."""
+    sp = SPATIAL if spatial_proxy == 0 else SLIDING
+    outs = {n: [] for n in ("full", "sink", "dummy", "spatial")}
+    for h in range(q.shape[0]):
+        outs["full"].append(attend_head(q[h], k[h], v[h], GLOBAL, geom, scale))
+        outs["sink"].append(attend_head(q[h], k[h], v[h], SINK, geom, scale))
+        outs["dummy"].append(attend_head(q[h], k[h], v[h], DUMMY, geom, scale))
+        outs["spatial"].append(attend_head(q[h], k[h], v[h], sp, geom, scale, radius=radius))
+    return {n: np.stack(o) for n, o in outs.items()}
+
+
+def head_scores(o_full, o_sink, o_dummy, o_spatial, params: ClassifyParams = ClassifyParams()):
+    """Per-head diagnostics [C_sink, C_dummy, C_spatial, S_score] from one
+    head's four outputs (each [Nq, d]), plus the per-query cosines [3, Nq]."""
+    c = np.stack([cosine_rows(o_full, o_sink),
+                  cosine_rows(o_full, o_dummy),
+                  cosine_rows(o_full, o_spatial)])
+    diff = np.asarray(o_full, dtype=np.float64) - np.asarray(o_spatial, dtype=np.float64)
+    mse = float(np.mean(diff * diff))
+    s_score = percentile_linear(c[2], params.percentile) - params.gamma * mse
+    diag = np.array([c[0].mean(), c[1].mean(), c[2].mean(), s_score])
+    return diag, c, mse
+
+
+def decide_label(diag, params: ClassifyParams = ClassifyParams()) -> int:
+    """Routing rule: which proxies clear their thresholds, then pick one."""
+    c_sink, c_dummy, c_sp, s_sc = (float(x) for x in diag)
+    cleared = []
+    if c_sink >= params.theta_sink:
+        cleared.append((SINK, c_sink))
+    if c_dummy >= params.theta_dummy:
+        cleared.append((DUMMY, c_dummy))
+    if c_sp >= params.theta_spatial and s_sc >= params.theta_score:
+        cleared.append((SPATIAL, c_sp))
+    if not cleared:
+        return GLOBAL
+    if params.rule == 1:
+        return cleared[0][0]
+    best = cleared[0]
+    for lab, val in cleared[1:]:   # strict '>' keeps the earlier archetype on ties
+        if val > best[1]:
+            best = (lab, val)
+    return best[0]
+
+
+def decision_margin(diag, params: ClassifyParams = ClassifyParams()) -> float:
+    """Smallest distance of any quantity the rule compares from the value at
+    which the decision would flip; labels are only comparable bit-for-bit
+    between two implementations when this exceeds their numeric error."""
+    c_sink, c_dummy, c_sp, s_sc = (float(x) for x in diag)
+    gaps = [abs(c_sink - params.theta_sink), abs(c_dummy - params.theta_dummy),
+            abs(c_sp - params.theta_spatial), abs(s_sc - params.theta_score)]
+    if params.rule == 0:
+        vals = []
+        if c_sink >= params.theta_sink:
+            vals.append(c_sink)
+        if c_dummy >= params.theta_dummy:
+            vals.append(c_dummy)
+        if c_sp >= params.theta_spatial and s_sc >= params.theta_score:
+            vals.append(c_sp)
+        vals.sort(reverse=True)
+        if len(vals) >= 2:
+            gaps.append(vals[0] - vals[1])
+    return min(gaps)
+
+
+def classify_head(q, k, v, geom: Geometry, params: ClassifyParams = ClassifyParams(),
+                  scale: float | None = None):
+    """One head: (label, diag [4], per-query cosines [3, Nq], mse)."""
+    sp = SPATIAL if params.spatial_proxy == 0 else SLIDING
+    o_full = attend_head(q, k, v, GLOBAL, geom, scale)
+    o_sink = attend_head(q, k, v, SINK, geom, scale)
+    o_dummy = attend_head(q, k, v, DUMMY, geom, scale)
+    o_sp = attend_head(q, k, v, sp, geom, scale, radius=params.radius)
+    diag, cos, mse = head_scores(o_full, o_sink, o_dummy, o_sp, params)
+    return decide_label(diag, params), diag, cos, mse
+
+
+def classify(q, k, v, geom: Geometry, params: ClassifyParams = ClassifyParams(),
+             scale: float | None = None):
+    """All heads: labels int8 [H], diag [H, 4]."""
+    labels, diags = [], []
+    for h in range(q.shape[0]):
+        lab, diag, _, _ = classify_head(q[h], k[h], v[h], geom, params, scale)
+        labels.append(lab)
+        diags.append(diag)
+    return np.array(labels, dtype=np.int8), np.stack(diags)
+
+
+# ----------------------------------------------------------------------------
+# Restructured cache: an index model of the per-archetype buffers.
+# ----------------------------------------------------------------------------
+PUSH_BLOCK, REPLACE_NEWEST = 0, 1
+
+
+class CacheModel:
+    """What each per-archetype buffer must hold after a sequence of appends.
+
+    Physical layout (the library's documented layout, restated from its
+    definition, not from its code):
+      * heads of one archetype get slots 0, 1, ... in ascending head order;
+      * Global  [slot][W*T][d]: a ring of W/B block slots; block b lives in
+        ring slot b mod (W/B), rows in frame-major token order;
+      * Sink    [slot][B*T][d]: block 0, written once;
+      * Dummy   [slot][B*T][d]: the newest block;
+      * Spatial [slot][W*T][d]: cell-major.  Cell c starts at row
+        W * sum_{c' < c} |c'|; inside it, frame slot s (0..W-1) holds |c|
+        rows in row-major (y, x) order; frame i of block b goes to frame
+        slot (b mod (W/B)) * B + i.
+    Rows never written are unspecified and reported as invalid."""
+
+    def __init__(self, geom: Geometry, labels):
+        assert geom.window_frames % geom.block_frames == 0
+        self.g = geom
+        self.labels = np.asarray(labels, dtype=np.int64)
+        self.nb = geom.window_frames // geom.block_frames
+        self.blocks_k: list = []      # chronological list of [H][B*T][d] blocks
+        self.blocks_v: list = []
+        self.sink_k = None
+        self.sink_v = None
+
+    @property
+    def n_appended(self) -> int:
+        return len(self.blocks_k)
+
+    def append(self, k_block, v_block, mode: int = PUSH_BLOCK):
+        if mode == PUSH_BLOCK:
+            self.blocks_k.append(np.array(k_block, copy=True))
+            self.blocks_v.append(np.array(v_block, copy=True))
+        elif mode == REPLACE_NEWEST:
+            if not self.blocks_k:
+                raise ValueError("REPLACE_NEWEST before any block")
+            self.blocks_k[-1] = np.array(k_block, copy=True)
+            self.blocks_v[-1] = np.array(v_block, copy=True)
+        else:
+            raise ValueError(mode)
+        if len(self.blocks_k) == 1:   # block 0 is the sink block (also when replaced)
+            self.sink_k = self.blocks_k[0]
+            self.sink_v = self.blocks_v[0]
+
+    def window(self):
+        """Logical window (k, v) [H, nf*T, d], oldest block first: the last
+        min(n, W/B) blocks appended."""
+        ks = self.blocks_k[-self.nb:]
+        vs = self.blocks_v[-self.nb:]
+        return np.concatenate(ks, axis=1), np.concatenate(vs, axis=1)
+
+    def slots(self, label: int):
+        return [h for h in range(self.labels.size) if self.labels[h] == label]
+
+    def expected_buffer(self, label: int, which: str):
+        """(data [n_slots, rows, d], valid [rows] bool) of one buffer."""
+        g, nb, B, T = self.g, self.nb, self.g.block_frames, self.g.T
+        heads = self.slots(label)
+        blocks = self.blocks_k if which == "k" else self.blocks_v
+        sample = blocks[0]
+        d = sample.shape[2]
+        n = len(blocks)
+        if label in (SINK, DUMMY):
+            src = (self.sink_k if which == "k" else self.sink_v) if label == SINK else blocks[-1]
+            data = np.stack([src[h] for h in heads]) if heads else np.zeros((0, B * T, d), sample.dtype)
+            return data, np.ones(B * T, dtype=bool)
+        rows = g.window_frames * T
+        data = np.zeros((len(heads), rows, d), dtype=sample.dtype)
+        valid = np.zeros(rows, dtype=bool)
+        for b in range(max(0, n - nb), n):
+            slot = b % nb
+            blk = blocks[b]
+            if label == GLOBAL:
+                r0 = slot * B * T
+                for s, h in enumerate(heads):
+                    data[s, r0:r0 + B * T] = blk[h]
+                valid[r0:r0 + B * T] = True
+            elif label == SPATIAL:
+                base = 0
+                for c in range(g.n_cells):
+                    y0, y1, x0, x1 = g.cell_box(c)
+                    size = (y1 - y0) * (x1 - x0)
+                    for i in range(B):
+                        fs = slot * B + i
+                        r0 = base + fs * size
+                        toks = [i * T + y * g.grid_w + x for y in range(y0, y1) for x in range(x0, x1)]
+                        for s, h in enumerate(heads):
+                            data[s, r0:r0 + size] = blk[h][toks]
+                        valid[r0:r0 + size] = True
+                    base += g.window_frames * size
+            else:
+                raise ValueError(label)
+        return data, valid
+
+
+# ----------------------------------------------------------------------------
+# Algorithmic work (what the method must compute / move), used for roofline
+# accounting by the benchmark's CPU leg and by tests of the accounting.
+# ----------------------------------------------------------------------------
+def keyset_sizes(geom: Geometry, pathway: int, n_frames: int | None = None) -> int:
+    """sum over queries of |S(i)| for one head."""
+    nf = geom.window_frames if n_frames is None else n_frames
+    B, T = geom.block_frames, geom.T
+    if pathway == GLOBAL:
+        return B * T * nf * T
+    if pathway in (SINK, DUMMY):
+        return B * T * B * T
+    if pathway == SPATIAL:
+        return sum(B * geom.cell_size(c) * nf * geom.cell_size(c) for c in range(geom.n_cells))
+    raise ValueError(pathway)
