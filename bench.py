@@ -1,0 +1,276 @@
+"""Benchmark: head-routed attention query-heads/s per layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 720p]
+
+One step = one steady-state denoising step of one layer: the block being
+denoised gets new keys/values (hc_cache_append with REPLACE_NEWEST) and every
+head attends over its archetype's keys (hc_attend).  Inputs are synthetic
+N(0,1) bf16 of the workload's shape, resident in HBM before timing starts;
+the cache is restructured (W/B block appends) before timing.
+
+Prints ONE JSON line with the metric, the roofline of the dominant kernel
+(the attention kernel, timed with HIP events on the stream it runs on), the
+same GPU's full-attention time (every head Global) and the CPU oracle timed
+on a bounded sample."""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def cell_sizes(gh, gw, ch=10, cw=10):
+    out = []
+    for cy in range(-(-gh // ch)):
+        for cx in range(-(-gw // cw)):
+            out.append(min(ch, gh - cy * ch) * min(cw, gw - cx * cw))
+    return out
+
+
+def algorithmic_work(wl, labels):
+    """Per pathway: (flops, bytes) a layer must compute / move.  Flops are
+    4*d per (query, key) pair of each head's key set (QK^T and PV); bytes are
+    Q read + O written + each head's K/V set read once (bf16)."""
+    B, W, T, d, Nq = wl.block_frames, wl.window_frames, wl.T, wl.head_dim, wl.Nq
+    pairs = {3: Nq * W * T, 0: Nq * B * T, 1: Nq * B * T,
+             2: B * W * sum(c * c for c in cell_sizes(wl.grid_h, wl.grid_w))}
+    keys = {3: W * T, 0: B * T, 1: B * T, 2: W * T}
+    out = {}
+    for lab in (0, 1, 2, 3):
+        n = int(sum(1 for x in labels if int(x) == lab))
+        out[lab] = (n * 4 * d * pairs[lab], n * (2 * 2 * Nq * d + 2 * 2 * keys[lab] * d))
+    return out
+
+
+def gen_inputs(wl, seed, device):
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    mk = lambda n: torch.randn(wl.heads, n, wl.head_dim, generator=g, device=device,
+                               dtype=torch.float32).to(torch.bfloat16)
+    return mk(wl.Nq), mk(wl.Nk), mk(wl.Nk)
+
+
+class Layer:
+    """One layer's restructured cache plus its inputs."""
+
+    def __init__(self, wl, labels, q, k, v):
+        import head_routed_kv_amd as hk
+        self.hk = hk
+        cfg = hk.make_config(wl.heads, wl.head_dim, wl.grid_h, wl.grid_w, wl.block_frames, wl.window_frames)
+        self.cache = hk.RoutedCache(cfg, [int(x) for x in labels])
+        BT = wl.Nq
+        for b in range(wl.n_blocks):
+            self.cache.append(k[:, b * BT:(b + 1) * BT], v[:, b * BT:(b + 1) * BT])
+        self.q = q
+        self.k_new = k[:, (wl.n_blocks - 1) * BT:]
+        self.v_new = v[:, (wl.n_blocks - 1) * BT:]
+        import torch
+        self.out = torch.empty_like(q)
+
+    def append(self):
+        self.cache.append(self.k_new, self.v_new, self.hk.HC_REPLACE_NEWEST)
+
+    def attend(self):
+        self.cache.attend(self.q, self.out)
+
+    def step(self):
+        self.append()
+        self.attend()
+
+
+def time_events(fn, iters, flush=None):
+    """Average ms of fn() between HIP events on the current stream."""
+    import torch
+    total = 0.0
+    for _ in range(iters):
+        if flush is not None:
+            flush()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        b.synchronize()
+        total += a.elapsed_time(b)
+    return total / iters
+
+
+def make_flush(device):
+    import torch
+    buf = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=device)
+
+    def flush():   # write 512 MiB so the 256 MB Infinity Cache holds none of the layer's K/V
+        buf.fill_(1.0)
+    return flush
+
+
+def cpu_baseline(wl, labels, seed, budget_s=20.0):
+    """The oracle (fp64 numpy) on a bounded sample: every head, a seeded
+    sample of query rows, timed on this host."""
+    import numpy as np
+    from head_routed_kv_amd import workloads as W
+    from oracle import headcast_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = 1
+    data = W.window(wl, seed=seed)
+    fq, fk, fv = (W.as_float(data[n], wl) for n in ("q", "k", "v"))
+    g = O.Geometry(wl.grid_h, wl.grid_w, wl.block_frames, wl.window_frames)
+    rng = np.random.default_rng(seed)
+    rows_per_head = 16
+    done_rows, t0 = 0, time.perf_counter()
+    while True:
+        rows = np.sort(rng.choice(wl.Nq, rows_per_head, replace=False))
+        O.routed_attention(fq, fk, fv, np.asarray(labels), g, rows=rows)
+        done_rows += rows_per_head
+        el = time.perf_counter() - t0
+        if el > budget_s or done_rows >= 512:
+            break
+    qh = done_rows * wl.heads
+    return {"value": qh / el, "unit": "query-heads/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{wl.name}: all {wl.heads} heads, {done_rows} seeded query rows per head "
+                      f"({qh} query-heads) of the routed layer, fp64 numpy, {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="720p")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-extra", action="store_true", help="skip the 1080p and per-pathway figures")
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {a.gpus}). "
+              "Heads shard across GPUs with no exchange in attention; run one process per GPU.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import head_routed_kv_amd as hk
+    from head_routed_kv_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    wl = W.WORKLOADS[a.workload]
+    labels = W.make_labels(wl, a.seed)
+    q, k, v = gen_inputs(wl, a.seed, dev)
+    layer = Layer(wl, labels, q, k, v)
+    torch.cuda.synchronize()
+
+    for _ in range(a.warmup):
+        layer.step()
+    torch.cuda.synchronize()
+    # timed region: exactly K steps; HIP events on the same stream bracket each hc_attend
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        layer.append()
+        evs[i][0].record()
+        layer.attend()
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / a.steps
+    attend_ms = sum(s.elapsed_time(e) for s, e in evs) / a.steps
+
+    work = algorithmic_work(wl, labels)
+    flops = sum(f for f, _ in work.values())
+    value = wl.heads * wl.Nq / (ms_step / 1e3)
+    achieved = flops / (attend_ms / 1e3) / 1e12
+
+    flush = make_flush(dev)
+    cold_ms = time_events(layer.attend, 10, flush)
+    # full-attention baseline on the same GPU: every head Global, same inputs
+    full = Layer(wl, [3] * wl.heads, q, k, v)
+    for _ in range(3):
+        full.attend()
+    full_ms = time_events(full.attend, 10)
+    full_cold_ms = time_events(full.attend, 5, flush)
+    full_flops = wl.heads * 4 * wl.head_dim * wl.Nq * wl.Nk
+    del full
+
+    extra = {}
+    if not a.no_extra:
+        # each pathway group alone: a cache holding only that group's heads
+        for lab, name in ((3, "global"), (0, "sink"), (1, "dummy"), (2, "spatial")):
+            heads = [h for h in range(wl.heads) if int(labels[h]) == lab]
+            if not heads:
+                continue
+            sub = W.small(wl, heads=len(heads))
+            idx = torch.tensor(heads, device=dev)
+            lay = Layer(sub, [lab] * len(heads), q[idx].contiguous(), k[idx].contiguous(), v[idx].contiguous())
+            for _ in range(3):
+                lay.attend()
+            ms = time_events(lay.attend, 10, flush)
+            f, by = work[lab]
+            extra[name] = {"heads": len(heads), "ms_cold": round(ms, 4),
+                           "tflops": round(f / (ms / 1e3) / 1e12, 1), "mfma_frac": round(f / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                           "hbm_gbs": round(by / (ms / 1e3) / 1e9, 1), "hbm_frac": round(by / (ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4)}
+            del lay
+        del layer, q, k, v
+        torch.cuda.empty_cache()
+        # 1080p layer
+        wl2 = W.WORKLOADS["1080p"]
+        lab2 = W.make_labels(wl2, a.seed)
+        q2, k2, v2 = gen_inputs(wl2, a.seed + 1, dev)
+        l2 = Layer(wl2, lab2, q2, k2, v2)
+        for _ in range(2):
+            l2.step()
+        ms2 = time_events(l2.step, 5)
+        at2 = time_events(l2.attend, 5)
+        f2 = sum(f for f, _ in algorithmic_work(wl2, lab2).values())
+        extra["1080p"] = {"ms_per_step": round(ms2, 3), "query_heads_per_s": round(wl2.heads * wl2.Nq / (ms2 / 1e3)),
+                          "attend_ms": round(at2, 3), "tflops": round(f2 / (at2 / 1e3) / 1e12, 1),
+                          "mfma_frac": round(f2 / (at2 / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        del l2, q2, k2, v2
+
+    cpu = None
+    if not a.no_cpu:
+        cpu = cpu_baseline(wl, labels, a.seed)
+
+    line = {
+        "metric": "head-routed attention query-heads/sec per layer",
+        "value": round(value, 1),
+        "unit": "query-heads/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic N(0,1) bf16 Q/K/V (seeded), labels by the 25/40/20/15% Global/Spatial/Sink/Dummy mix",
+        "config": {"workload": f"{wl.name} routed layer", "heads": wl.heads, "head_dim": wl.head_dim,
+                   "grid": [wl.grid_h, wl.grid_w], "block_frames": wl.block_frames,
+                   "window_frames": wl.window_frames, "queries": wl.Nq, "keys": wl.Nk,
+                   "labels": [int(x) for x in labels], "step": "append(REPLACE_NEWEST) + attend"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "attn_bf16_kernel<128,false>", "attend_ms": round(attend_ms, 4),
+                     "algorithmic_flops": flops},
+        "attend_cold_ms": round(cold_ms, 4),
+        "full_attention": {"ms": round(full_ms, 4), "ms_cold": round(full_cold_ms, 4),
+                           "tflops": round(full_flops / (full_ms / 1e3) / 1e12, 1),
+                           "speedup_vs_full": round(full_ms / attend_ms, 3)},
+        "pathways": extra,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

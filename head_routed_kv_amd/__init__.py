@@ -1,0 +1,96 @@
+"""Head-routed attention (HeadCast) for AMD MI355X.
+
+The compute lives in libheadcast.so (HIP kernels for gfx950) behind the C ABI
+declared in include/headcast.h.  This package is its Python face:
+  * `_native`     ctypes binding, one function per C entry point, same names;
+  * `RoutedCache`, `classify`, `tensor_arg`   torch conveniences that only
+    allocate device memory with torch and pass pointers, strides and the
+    current HIP stream to the library;
+  * `workloads`   seeded synthetic inputs.
+"""
+from __future__ import annotations
+
+from . import _native
+from ._native import (HC_BF16, HC_DUMMY, HC_FP32, HC_GLOBAL, HC_PUSH_BLOCK, HC_REPLACE_NEWEST, HC_SINK,
+                      HC_SPATIAL, HeadcastError, hc_attend, hc_cache_append, hc_cache_bytes, hc_cache_create,
+                      hc_cache_destroy, hc_cache_get_layout, hc_classify, hc_classify_workspace_bytes,
+                      hc_default_classify_params, hc_last_error_message, hc_status_string, hc_validate_config,
+                      make_config)
+
+__all__ = ["RoutedCache", "classify", "tensor_arg", "make_config", "HeadcastError", "HC_BF16", "HC_FP32",
+           "HC_SINK", "HC_DUMMY", "HC_SPATIAL", "HC_GLOBAL", "HC_PUSH_BLOCK", "HC_REPLACE_NEWEST"]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def tensor_arg(t):
+    """(pointer, stride_head, stride_token) of a [H, N, d] tensor with
+    contiguous channels."""
+    if t.dim() != 3 or t.stride(2) != 1:
+        raise ValueError("expected a [heads, tokens, channels] tensor with contiguous channels")
+    return (t.data_ptr(), t.stride(0), t.stride(1))
+
+
+def _stream():
+    return _torch().cuda.current_stream().cuda_stream
+
+
+def torch_dtype(cfg):
+    torch = _torch()
+    return torch.bfloat16 if cfg.dtype == HC_BF16 else torch.float32
+
+
+class RoutedCache:
+    """A restructured KV cache for one layer: device memory from torch, all
+    work in the library."""
+
+    def __init__(self, cfg, labels, device="cuda"):
+        torch = _torch()
+        self.cfg = cfg
+        self.labels = [int(x) for x in labels]
+        self.nbytes = hc_cache_bytes(cfg, self.labels)
+        self.mem = torch.empty(max(self.nbytes, 256), dtype=torch.uint8, device=device)
+        self.handle = hc_cache_create(cfg, self.labels, self.mem.data_ptr(), self.mem.numel())
+
+    def append(self, k_block, v_block, mode=HC_PUSH_BLOCK):
+        hc_cache_append(self.handle, tensor_arg(k_block), tensor_arg(v_block), mode, _stream())
+
+    def attend(self, q_block, out=None):
+        if out is None:
+            out = _torch().empty_like(q_block)
+        hc_attend(self.handle, tensor_arg(q_block), tensor_arg(out), _stream())
+        return out
+
+    def layout(self):
+        return hc_cache_get_layout(self.handle)
+
+    def close(self):
+        if self.handle is not None:
+            hc_cache_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def classify(cfg, q_block, k_window, v_window, params=None, workspace=None):
+    """One-shot classifier.  Returns (labels int8 [H], diag fp32 [H,4],
+    workspace) as device tensors; the workspace holds the four outputs and
+    the per-query cosines (layout in include/headcast.h)."""
+    torch = _torch()
+    params = params or hc_default_classify_params()
+    H = cfg.num_heads
+    need = hc_classify_workspace_bytes(cfg)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q_block.device)
+    labels = torch.empty(H, dtype=torch.int8, device=q_block.device)
+    diag = torch.empty(H, 4, dtype=torch.float32, device=q_block.device)
+    hc_classify(cfg, params, tensor_arg(q_block), tensor_arg(k_window), tensor_arg(v_window),
+                workspace.data_ptr(), workspace.numel(), labels.data_ptr(), diag.data_ptr(), _stream())
+    return labels, diag, workspace

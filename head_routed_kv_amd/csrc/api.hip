@@ -1,0 +1,557 @@
+// Host side of libheadcast.so: argument checking, the restructured cache's
+// layout, work plans and kernel launches.  Allocates no device memory and
+// never synchronises the device.
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <functional>
+#include <new>
+#include <queue>
+#include <string>
+#include <vector>
+
+#include "hc_internal.h"
+
+using namespace hc;
+
+namespace {
+
+thread_local std::string g_err;
+
+hc_status fail(hc_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+hc_status hip_fail(hipError_t e, const char* what) {
+  return fail(HC_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t elt_size(int dtype) { return dtype == HC_BF16 ? 2 : 4; }
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+// The split plan is made for the 256 compute units of an MI355X, two work
+// groups of the attention kernel per compute unit.
+constexpr int kWorkGroupSlots = 256 * 2;
+constexpr int kMaxSplits = 8;
+
+hc_status check_config(const hc_config* c) {
+  if (!c) return fail(HC_ERR_INVALID_ARG, "config is NULL");
+  if (c->dtype != HC_BF16 && c->dtype != HC_FP32) return fail(HC_ERR_DTYPE, "dtype %d is not HC_BF16 or HC_FP32", c->dtype);
+  if (c->num_heads < 1 || c->num_heads > HC_MAX_HEADS)
+    return fail(HC_ERR_SHAPE, "num_heads %d outside 1..%d", c->num_heads, HC_MAX_HEADS);
+  if (c->head_dim != 64 && c->head_dim != 128) return fail(HC_ERR_SHAPE, "head_dim %d is not 64 or 128", c->head_dim);
+  if (c->grid_h < 1 || c->grid_w < 1) return fail(HC_ERR_SHAPE, "grid %dx%d is empty", c->grid_h, c->grid_w);
+  if (c->block_frames < 1 || c->window_frames < c->block_frames || c->window_frames % c->block_frames)
+    return fail(HC_ERR_SHAPE, "window_frames %d must be a positive multiple of block_frames %d", c->window_frames,
+                c->block_frames);
+  if (c->cell_h < 1 || c->cell_w < 1) return fail(HC_ERR_SHAPE, "cell %dx%d is empty", c->cell_h, c->cell_w);
+  const int64_t T = (int64_t)c->grid_h * c->grid_w;
+  if (T * c->window_frames * c->head_dim > (int64_t)1 << 31)
+    return fail(HC_ERR_SHAPE, "window of %lld tokens x %d channels is too large", (long long)(T * c->window_frames),
+                c->head_dim);
+  if (!(c->softmax_scale >= 0.f) || !std::isfinite(c->softmax_scale))
+    return fail(HC_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
+  return HC_OK;
+}
+
+hc_status check_tensor(const void* ptr, int64_t sh, int64_t st, const hc_config* c, const char* name) {
+  const size_t e = elt_size(c->dtype);
+  if (!ptr) return fail(HC_ERR_INVALID_ARG, "%s: NULL pointer", name);
+  if ((uintptr_t)ptr % 16) return fail(HC_ERR_ALIGN, "%s: pointer not 16-byte aligned", name);
+  if (st < c->head_dim) return fail(HC_ERR_SHAPE, "%s: token stride %lld < head_dim", name, (long long)st);
+  if (sh < 0) return fail(HC_ERR_SHAPE, "%s: negative head stride", name);
+  if ((st * (int64_t)e) % 16 || (sh * (int64_t)e) % 16)
+    return fail(HC_ERR_ALIGN, "%s: strides must be multiples of 16 bytes", name);
+  return HC_OK;
+}
+
+float softmax_scale(const hc_config* c) {
+  return c->softmax_scale > 0.f ? c->softmax_scale : 1.0f / std::sqrt((float)c->head_dim);
+}
+
+struct Geom {
+  int T, Nq, Nk, nb, q_tiles, n_cells, cell_cols, cell_subtiles;
+  std::vector<int> cell_size;
+};
+
+Geom geometry(const hc_config* c) {
+  Geom g;
+  g.T = c->grid_h * c->grid_w;
+  g.Nq = c->block_frames * g.T;
+  g.Nk = c->window_frames * g.T;
+  g.nb = c->window_frames / c->block_frames;
+  g.q_tiles = cdiv(g.Nq, QTILE);
+  const int rows = cdiv(c->grid_h, c->cell_h);
+  g.cell_cols = cdiv(c->grid_w, c->cell_w);
+  g.n_cells = rows * g.cell_cols;
+  const int max_cell = std::min(c->cell_h, c->grid_h) * std::min(c->cell_w, c->grid_w);
+  g.cell_subtiles = cdiv((int64_t)c->block_frames * max_cell, QTILE);
+  for (int cy = 0; cy < rows; ++cy)
+    for (int cx = 0; cx < g.cell_cols; ++cx) {
+      const int h = std::min(c->cell_h, c->grid_h - cy * c->cell_h);
+      const int w = std::min(c->cell_w, c->grid_w - cx * c->cell_w);
+      g.cell_size.push_back(h * w);
+    }
+  return g;
+}
+
+// List-schedule the units of a full-window layer onto the work-group slots
+// (heaviest category first, as the kernel numbers them) and return the
+// makespan in key tiles.  Used to pick how many key-range splits the Global
+// heads get: enough units to keep every slot busy, not so many that the
+// partial-merge traffic dominates.
+double simulate(const hc_config* c, const Geom& g, const int count[4], int splits) {
+  std::priority_queue<double, std::vector<double>, std::greater<double>> slots;
+  for (int i = 0; i < kWorkGroupSlots; ++i) slots.push(0.0);
+  auto run = [&](double cost, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) {
+      const double t = slots.top();
+      slots.pop();
+      slots.push(t + cost);
+    }
+  };
+  const int key_tiles = cdiv(g.Nk, KTILE);
+  const int kps_tiles = cdiv(key_tiles, splits);
+  const double fixed = 2.0;  // per-unit set-up and write-back, in key tiles
+  run(kps_tiles + fixed + (splits > 1 ? 0.5 * splits : 0.0), (int64_t)count[HC_GLOBAL] * g.q_tiles * splits);
+  run(cdiv(g.Nq, KTILE) + fixed, (int64_t)(count[HC_SINK] + count[HC_DUMMY]) * g.q_tiles);
+  for (int h = 0; h < count[HC_SPATIAL]; ++h)
+    for (int cl = 0; cl < g.n_cells; ++cl) {
+      const int qall = c->block_frames * g.cell_size[cl];
+      const int sub = cdiv(qall, QTILE);
+      run(cdiv((int64_t)c->window_frames * g.cell_size[cl], KTILE) + fixed, sub);
+    }
+  double mk = 0;
+  while (!slots.empty()) {
+    mk = std::max(mk, slots.top());
+    slots.pop();
+  }
+  return mk;
+}
+
+int choose_splits(const hc_config* c, const Geom& g, const int count[4]) {
+  if (c->dtype != HC_BF16 || count[HC_GLOBAL] == 0) return 1;
+  int best = 1;
+  double best_t = simulate(c, g, count, 1);
+  for (int s = 2; s <= kMaxSplits; ++s) {
+    if (cdiv(g.Nk, KTILE) < 4 * s) break;  // each split keeps at least 4 key tiles
+    const double t = simulate(c, g, count, s);
+    if (t < 0.97 * best_t) {
+      best = s;
+      best_t = t;
+    }
+  }
+  return best;
+}
+
+struct Layout {
+  int count[4] = {0, 0, 0, 0};
+  int slot[HC_MAX_HEADS];
+  uint8_t head_of[4][HC_MAX_HEADS];
+  size_t off_k[4], off_v[4], slot_bytes[4];
+  size_t off_part = 0, off_counters = 0, scratch_bytes = 0, total = 0;
+  int splits = 1;
+  int64_t n_counters = 0;
+};
+
+hc_status make_layout(const hc_config* c, const int8_t* labels, Layout* L) {
+  hc_status st = check_config(c);
+  if (st) return st;
+  if (!labels) return fail(HC_ERR_INVALID_ARG, "labels is NULL");
+  for (int h = 0; h < c->num_heads; ++h) {
+    const int lab = labels[h];
+    if (lab < HC_SINK || lab > HC_GLOBAL) return fail(HC_ERR_INVALID_ARG, "label of head %d is %d, not 0..3", h, lab);
+    L->slot[h] = L->count[lab];
+    L->head_of[lab][L->count[lab]++] = (uint8_t)h;
+  }
+  const Geom g = geometry(c);
+  const size_t row = (size_t)c->head_dim * elt_size(c->dtype);
+  L->slot_bytes[HC_GLOBAL] = L->slot_bytes[HC_SPATIAL] = (size_t)g.Nk * row;
+  L->slot_bytes[HC_SINK] = L->slot_bytes[HC_DUMMY] = (size_t)g.Nq * row;
+  size_t off = 0;
+  for (int lab : {HC_GLOBAL, HC_SINK, HC_DUMMY, HC_SPATIAL}) {
+    L->off_k[lab] = off;
+    off = align256(off + L->count[lab] * L->slot_bytes[lab]);
+    L->off_v[lab] = off;
+    off = align256(off + L->count[lab] * L->slot_bytes[lab]);
+  }
+  L->splits = choose_splits(c, g, L->count);
+  L->off_part = off;
+  if (L->splits > 1) {
+    const int64_t ids = (int64_t)L->count[HC_GLOBAL] * g.q_tiles;
+    const size_t part = (size_t)ids * L->splits * QTILE * ((size_t)c->head_dim + 2) * sizeof(float);
+    L->off_counters = align256(off + part);
+    L->n_counters = ids;
+    off = align256(L->off_counters + ids * sizeof(int32_t));
+  } else {
+    L->off_counters = off;
+  }
+  L->scratch_bytes = off - L->off_part;
+  L->total = off;
+  return HC_OK;
+}
+
+}  // namespace
+
+struct hc_cache {
+  hc_config cfg;
+  int8_t labels[HC_MAX_HEADS];
+  Layout L;
+  uint8_t* dev = nullptr;
+  size_t bytes = 0;
+  int n_appended = 0;
+  bool counters_zeroed = false;
+};
+
+extern "C" {
+
+void hc_default_classify_params(hc_classify_params* p) {
+  if (!p) return;
+  p->theta_sink = 0.95f;
+  p->theta_dummy = 0.95f;
+  p->theta_spatial = 0.95f;
+  p->theta_score = 0.755f;
+  p->gamma = 5.0f;
+  p->percentile = 5.0f;
+  p->rule = 0;
+  p->spatial_proxy = 0;
+  p->radius = 2;
+}
+
+hc_status hc_validate_config(const hc_config* cfg) { return check_config(cfg); }
+
+hc_status hc_cache_bytes(const hc_config* cfg, const int8_t* labels_host, size_t* device_bytes) {
+  if (!device_bytes) return fail(HC_ERR_INVALID_ARG, "device_bytes is NULL");
+  Layout L;
+  hc_status st = make_layout(cfg, labels_host, &L);
+  if (st) return st;
+  *device_bytes = L.total;
+  return HC_OK;
+}
+
+hc_status hc_cache_create(const hc_config* cfg, const int8_t* labels_host, void* device_mem, size_t bytes,
+                          hc_cache** out) {
+  if (!out) return fail(HC_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  Layout L;
+  hc_status st = make_layout(cfg, labels_host, &L);
+  if (st) return st;
+  if (!device_mem) return fail(HC_ERR_INVALID_ARG, "device_mem is NULL");
+  if ((uintptr_t)device_mem % 256) return fail(HC_ERR_ALIGN, "device_mem must be 256-byte aligned");
+  if (bytes < L.total) return fail(HC_ERR_WORKSPACE, "cache needs %zu bytes, got %zu", L.total, bytes);
+  hc_cache* c = new (std::nothrow) hc_cache;
+  if (!c) return fail(HC_ERR_INVALID_ARG, "out of host memory");
+  c->cfg = *cfg;
+  std::memcpy(c->labels, labels_host, cfg->num_heads);
+  c->L = L;
+  c->dev = (uint8_t*)device_mem;
+  c->bytes = bytes;
+  *out = c;
+  return HC_OK;
+}
+
+hc_status hc_cache_destroy(hc_cache* cache) {
+  if (!cache) return fail(HC_ERR_INVALID_ARG, "cache is NULL");
+  delete cache;
+  return HC_OK;
+}
+
+hc_status hc_cache_get_layout(const hc_cache* c, hc_cache_layout* out) {
+  if (!c || !out) return fail(HC_ERR_INVALID_ARG, "NULL argument");
+  std::memset(out, 0, sizeof *out);
+  out->total_bytes = c->L.total;
+  out->off_global_k = c->L.off_k[HC_GLOBAL];
+  out->off_global_v = c->L.off_v[HC_GLOBAL];
+  out->off_sink_k = c->L.off_k[HC_SINK];
+  out->off_sink_v = c->L.off_v[HC_SINK];
+  out->off_dummy_k = c->L.off_k[HC_DUMMY];
+  out->off_dummy_v = c->L.off_v[HC_DUMMY];
+  out->off_spatial_k = c->L.off_k[HC_SPATIAL];
+  out->off_spatial_v = c->L.off_v[HC_SPATIAL];
+  out->off_scratch = c->L.off_part;
+  out->scratch_bytes = c->L.scratch_bytes;
+  out->n_global = c->L.count[HC_GLOBAL];
+  out->n_sink = c->L.count[HC_SINK];
+  out->n_dummy = c->L.count[HC_DUMMY];
+  out->n_spatial = c->L.count[HC_SPATIAL];
+  out->blocks_appended = c->n_appended;
+  out->global_splits = c->L.splits;
+  for (int h = 0; h < c->cfg.num_heads; ++h) out->head_slot[h] = c->L.slot[h];
+  return HC_OK;
+}
+
+hc_status hc_cache_append(hc_cache* c, hc_tensor k_block, hc_tensor v_block, int32_t mode, hipStream_t stream) {
+  if (!c) return fail(HC_ERR_INVALID_ARG, "cache is NULL");
+  if (mode != HC_PUSH_BLOCK && mode != HC_REPLACE_NEWEST) return fail(HC_ERR_INVALID_ARG, "mode %d", mode);
+  const hc_config* cfg = &c->cfg;
+  hc_status st = check_tensor(k_block.ptr, k_block.stride_head, k_block.stride_token, cfg, "k_block");
+  if (st) return st;
+  st = check_tensor(v_block.ptr, v_block.stride_head, v_block.stride_token, cfg, "v_block");
+  if (st) return st;
+  if (k_block.stride_head != v_block.stride_head || k_block.stride_token != v_block.stride_token)
+    return fail(HC_ERR_SHAPE, "k_block and v_block must share strides");
+  if (mode == HC_REPLACE_NEWEST && c->n_appended == 0) return fail(HC_ERR_STATE, "REPLACE_NEWEST before any block");
+  const Geom g = geometry(cfg);
+  const int b = (mode == HC_PUSH_BLOCK) ? c->n_appended : c->n_appended - 1;
+  const size_t e = elt_size(cfg->dtype);
+
+  if (c->L.splits > 1 && !c->counters_zeroed) {
+    hipError_t err = launch_fill_zero((int32_t*)(c->dev + c->L.off_counters), c->L.n_counters, stream);
+    if (err != hipSuccess) return hip_fail(err, "zeroing split counters");
+    c->counters_zeroed = true;
+  }
+
+  AppendPlan P;
+  std::memset(&P, 0, sizeof P);
+  P.k = (const uint8_t*)k_block.ptr;
+  P.v = (const uint8_t*)v_block.ptr;
+  P.src_sh = k_block.stride_head * (int64_t)e;
+  P.src_st = k_block.stride_token * (int64_t)e;
+  P.row_bytes = cfg->head_dim * (int)e;
+  P.rows = g.Nq;
+  P.H = cfg->num_heads;
+  P.T = g.T;
+  P.grid_w = cfg->grid_w;
+  P.grid_h = cfg->grid_h;
+  P.cell_h = cfg->cell_h;
+  P.cell_w = cfg->cell_w;
+  P.cell_cols = g.cell_cols;
+  P.B = cfg->block_frames;
+  P.W = cfg->window_frames;
+  P.ring_slot = b % g.nb;
+  P.write_sink = (b == 0);
+  for (int lab = 0; lab < 4; ++lab) {
+    P.dst_k[lab] = c->dev + c->L.off_k[lab];
+    P.dst_v[lab] = c->dev + c->L.off_v[lab];
+    P.dst_slot_bytes[lab] = (int64_t)c->L.slot_bytes[lab];
+  }
+  for (int h = 0; h < cfg->num_heads; ++h) {
+    P.label[h] = (uint8_t)c->labels[h];
+    P.slot[h] = (uint8_t)c->L.slot[h];
+  }
+  hipError_t err = launch_append(P, stream);
+  if (err != hipSuccess) return hip_fail(err, "append kernel launch");
+  if (mode == HC_PUSH_BLOCK) ++c->n_appended;
+  return HC_OK;
+}
+
+hc_status hc_attend(hc_cache* c, hc_tensor q, hc_out_tensor out, hipStream_t stream) {
+  if (!c) return fail(HC_ERR_INVALID_ARG, "cache is NULL");
+  const hc_config* cfg = &c->cfg;
+  hc_status st = check_tensor(q.ptr, q.stride_head, q.stride_token, cfg, "q_block");
+  if (st) return st;
+  st = check_tensor(out.ptr, out.stride_head, out.stride_token, cfg, "out");
+  if (st) return st;
+  if (out.ptr == q.ptr) return fail(HC_ERR_INVALID_ARG, "out aliases q_block");
+  if (c->n_appended < 1) return fail(HC_ERR_STATE, "hc_attend before any block was appended");
+  const Geom g = geometry(cfg);
+  const int nblk = std::min(c->n_appended, g.nb);
+  const bool bf16 = cfg->dtype == HC_BF16;
+
+  AttnPlan P;
+  std::memset(&P, 0, sizeof P);
+  P.q_tiles = g.q_tiles;
+  P.cell_subtiles = g.cell_subtiles;
+  P.q = q.ptr;
+  P.q_sh = q.stride_head;
+  P.q_st = q.stride_token;
+  P.T = g.T;
+  P.grid_w = cfg->grid_w;
+  P.grid_h = cfg->grid_h;
+  P.cell_h = cfg->cell_h;
+  P.cell_w = cfg->cell_w;
+  P.cell_cols = g.cell_cols;
+  P.B = cfg->block_frames;
+  P.W = cfg->window_frames;
+  P.Nq = g.Nq;
+  P.scale_log2 = softmax_scale(cfg) * 1.4426950408889634f;
+  const int64_t slot_elems[4] = {
+      (int64_t)(c->L.slot_bytes[0] / elt_size(cfg->dtype)), (int64_t)(c->L.slot_bytes[1] / elt_size(cfg->dtype)),
+      (int64_t)(c->L.slot_bytes[2] / elt_size(cfg->dtype)), (int64_t)(c->L.slot_bytes[3] / elt_size(cfg->dtype))};
+  int units = 0;
+  for (int lab : {HC_GLOBAL, HC_SINK, HC_DUMMY, HC_SPATIAL}) {
+    const int n = c->L.count[lab];
+    if (!n) continue;
+    AttnCat& C = P.cat[P.n_cats];
+    C.n_heads = n;
+    C.k = c->dev + c->L.off_k[lab];
+    C.v = c->dev + c->L.off_v[lab];
+    C.kv_sh = slot_elems[lab];
+    C.kv_st = cfg->head_dim;
+    C.o = out.ptr;
+    C.o_sh = out.stride_head;
+    C.o_st = out.stride_token;
+    C.out_f32 = bf16 ? 0 : 1;
+    C.unit_begin = units;
+    C.splits = 1;
+    if (lab == HC_SPATIAL) {
+      C.kind = KIND_CELL_MAJOR;
+      C.kv_count = nblk * cfg->block_frames;   // frames present
+      C.units_per_head = g.n_cells * g.cell_subtiles;
+    } else {
+      C.kind = KIND_RANGED;
+      C.kv_first = 0;
+      C.kv_count = (lab == HC_GLOBAL) ? nblk * g.Nq : g.Nq;
+      C.keys_per_split = C.kv_count;
+      if (lab == HC_GLOBAL && c->L.splits > 1) {
+        const int tiles = cdiv(C.kv_count, KTILE);
+        const int kps = cdiv(tiles, c->L.splits) * KTILE;
+        C.keys_per_split = kps;
+        C.splits = cdiv(C.kv_count, kps);
+        C.part = (float*)(c->dev + c->L.off_part);
+        C.counters = (int32_t*)(c->dev + c->L.off_counters);
+      }
+      C.units_per_head = g.q_tiles * C.splits;
+    }
+    for (int s = 0; s < n; ++s) P.head_of[P.n_cats][s] = c->L.head_of[lab][s];
+    units += n * C.units_per_head;
+    ++P.n_cats;
+  }
+  P.total_units = units;
+  hipError_t err = bf16 ? launch_attn_bf16(P, cfg->head_dim, stream) : launch_attn_f32(P, cfg->head_dim, stream);
+  if (err != hipSuccess) return hip_fail(err, "attention kernel launch");
+  return HC_OK;
+}
+
+hc_status hc_classify_workspace_bytes(const hc_config* cfg, size_t* bytes) {
+  if (!bytes) return fail(HC_ERR_INVALID_ARG, "bytes is NULL");
+  hc_status st = check_config(cfg);
+  if (st) return st;
+  const Geom g = geometry(cfg);
+  const size_t o = align256((size_t)4 * cfg->num_heads * g.Nq * cfg->head_dim * sizeof(float));
+  const size_t cs = align256((size_t)cfg->num_heads * 4 * g.Nq * sizeof(float));
+  *bytes = o + cs;
+  return HC_OK;
+}
+
+hc_status hc_classify(const hc_config* cfg, const hc_classify_params* prm, hc_tensor q, hc_tensor k_window,
+                      hc_tensor v_window, void* workspace, size_t ws_bytes, int8_t* labels_dev, float* diag_dev,
+                      hipStream_t stream) {
+  hc_status st = check_config(cfg);
+  if (st) return st;
+  if (!prm) return fail(HC_ERR_INVALID_ARG, "params is NULL");
+  if (prm->rule != 0 && prm->rule != 1) return fail(HC_ERR_INVALID_ARG, "rule %d", prm->rule);
+  if (prm->spatial_proxy == 1) return fail(HC_ERR_UNSUPPORTED, "the sliding-box Spatial proxy is not implemented");
+  if (prm->spatial_proxy != 0) return fail(HC_ERR_INVALID_ARG, "spatial_proxy %d", prm->spatial_proxy);
+  if (!(prm->percentile >= 0.f && prm->percentile <= 100.f)) return fail(HC_ERR_INVALID_ARG, "percentile outside 0..100");
+  if (!std::isfinite(prm->gamma)) return fail(HC_ERR_INVALID_ARG, "gamma is not finite");
+  if ((st = check_tensor(q.ptr, q.stride_head, q.stride_token, cfg, "q_block"))) return st;
+  if ((st = check_tensor(k_window.ptr, k_window.stride_head, k_window.stride_token, cfg, "k_window"))) return st;
+  if ((st = check_tensor(v_window.ptr, v_window.stride_head, v_window.stride_token, cfg, "v_window"))) return st;
+  if (k_window.stride_head != v_window.stride_head || k_window.stride_token != v_window.stride_token)
+    return fail(HC_ERR_SHAPE, "k_window and v_window must share strides");
+  if (!labels_dev || !diag_dev) return fail(HC_ERR_INVALID_ARG, "labels_dev / diag_dev is NULL");
+  if (!workspace) return fail(HC_ERR_INVALID_ARG, "workspace is NULL");
+  if ((uintptr_t)workspace % 256) return fail(HC_ERR_ALIGN, "workspace must be 256-byte aligned");
+  size_t need = 0;
+  hc_classify_workspace_bytes(cfg, &need);
+  if (ws_bytes < need) return fail(HC_ERR_WORKSPACE, "classifier needs %zu workspace bytes, got %zu", need, ws_bytes);
+
+  const Geom g = geometry(cfg);
+  const int H = cfg->num_heads, D = cfg->head_dim;
+  float* O = (float*)workspace;
+  float* Cc = (float*)((uint8_t*)workspace + align256((size_t)4 * H * g.Nq * D * sizeof(float)));
+  const int64_t plane = (int64_t)H * g.Nq * D;
+
+  AttnPlan P;
+  std::memset(&P, 0, sizeof P);
+  P.q_tiles = g.q_tiles;
+  P.cell_subtiles = g.cell_subtiles;
+  P.q = q.ptr;
+  P.q_sh = q.stride_head;
+  P.q_st = q.stride_token;
+  P.T = g.T;
+  P.grid_w = cfg->grid_w;
+  P.grid_h = cfg->grid_h;
+  P.cell_h = cfg->cell_h;
+  P.cell_w = cfg->cell_w;
+  P.cell_cols = g.cell_cols;
+  P.B = cfg->block_frames;
+  P.W = cfg->window_frames;
+  P.Nq = g.Nq;
+  P.scale_log2 = softmax_scale(cfg) * 1.4426950408889634f;
+  // outputs: 0 full, 1 sink, 2 dummy, 3 spatial
+  const int first[3] = {0, 0, g.Nk - g.Nq};
+  const int count[3] = {g.Nk, g.Nq, g.Nq};
+  int units = 0;
+  for (int k = 0; k < 4; ++k) {
+    AttnCat& C = P.cat[k];
+    C.n_heads = H;
+    C.k = k_window.ptr;
+    C.v = v_window.ptr;
+    C.kv_sh = k_window.stride_head;
+    C.kv_st = k_window.stride_token;
+    C.o = O + k * plane;
+    C.o_sh = (int64_t)g.Nq * D;
+    C.o_st = D;
+    C.out_f32 = 1;
+    C.splits = 1;
+    C.unit_begin = units;
+    if (k < 3) {
+      C.kind = KIND_RANGED;
+      C.kv_first = first[k];
+      C.kv_count = count[k];
+      C.keys_per_split = count[k];
+      C.units_per_head = g.q_tiles;
+    } else {
+      C.kind = KIND_CELL_GATHER;
+      C.kv_count = cfg->window_frames;
+      C.units_per_head = g.n_cells * g.cell_subtiles;
+    }
+    for (int h = 0; h < H; ++h) P.head_of[k][h] = (uint8_t)h;
+    units += H * C.units_per_head;
+  }
+  P.n_cats = 4;
+  P.total_units = units;
+  hipError_t err = cfg->dtype == HC_BF16 ? launch_attn_bf16(P, D, stream) : launch_attn_f32(P, D, stream);
+  if (err != hipSuccess) return hip_fail(err, "classifier attention launch");
+
+  CosPlan cp{O, Cc, H, g.Nq, D};
+  err = launch_cosines(cp, stream);
+  if (err != hipSuccess) return hip_fail(err, "classifier cosine launch");
+  ReducePlan rp;
+  rp.c = Cc;
+  rp.labels = labels_dev;
+  rp.diag = diag_dev;
+  rp.H = H;
+  rp.Nq = g.Nq;
+  rp.D = D;
+  rp.theta_sink = prm->theta_sink;
+  rp.theta_dummy = prm->theta_dummy;
+  rp.theta_spatial = prm->theta_spatial;
+  rp.theta_score = prm->theta_score;
+  rp.gamma = prm->gamma;
+  rp.percentile = prm->percentile;
+  rp.rule = prm->rule;
+  err = launch_classify_reduce(rp, stream);
+  if (err != hipSuccess) return hip_fail(err, "classifier reduce launch");
+  return HC_OK;
+}
+
+const char* hc_status_string(hc_status s) {
+  switch (s) {
+    case HC_OK: return "HC_OK";
+    case HC_ERR_INVALID_ARG: return "HC_ERR_INVALID_ARG";
+    case HC_ERR_SHAPE: return "HC_ERR_SHAPE";
+    case HC_ERR_DTYPE: return "HC_ERR_DTYPE";
+    case HC_ERR_ALIGN: return "HC_ERR_ALIGN";
+    case HC_ERR_WORKSPACE: return "HC_ERR_WORKSPACE";
+    case HC_ERR_STATE: return "HC_ERR_STATE";
+    case HC_ERR_HIP: return "HC_ERR_HIP";
+    case HC_ERR_UNSUPPORTED: return "HC_ERR_UNSUPPORTED";
+  }
+  return "HC_ERR_UNKNOWN";
+}
+
+const char* hc_last_error_message(void) { return g_err.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,112 @@
+// Internal declarations shared by the HIP sources of libheadcast.so.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/headcast.h"
+
+namespace hc {
+
+// ---------------------------------------------------------------------------
+// Attention work plan, passed by value as a kernel argument.
+//
+// The work of one launch is a list of "categories" (at most 4).  Every head of
+// a category has the same number of work units and the same key-set shape:
+//   RANGED       keys are a contiguous row range [kv_first, kv_first+kv_count)
+//                of the head's K/V matrix (Global, Sink, Dummy pathways);
+//   CELL_MAJOR   Spatial pathway over a cell-major buffer: cell c's keys are
+//                rows [W*off_c, W*off_c + nf*|c|);
+//   CELL_GATHER  Spatial pathway over a frame-major window: the keys of cell c
+//                in frames 0..nf-1 are gathered row by row.
+// Units are numbered category by category (heaviest first), head by head.
+// Ranged units are (split, q-tile) pairs, split-major, so that work groups
+// running at the same time on one XCD share the same key rows in L2.  Spatial
+// units are (cell, q-sub-tile) pairs; sub-tiles past a small cell are empty.
+// ---------------------------------------------------------------------------
+enum : int32_t { KIND_RANGED = 0, KIND_CELL_MAJOR = 1, KIND_CELL_GATHER = 2 };
+
+constexpr int QTILE = 128;  // queries per work group (4 waves x 32)
+constexpr int KTILE = 64;   // keys per inner iteration
+
+struct AttnCat {
+  int32_t kind;
+  int32_t n_heads;
+  int32_t units_per_head;
+  int32_t unit_begin;
+  int32_t kv_first;       // RANGED: first key row
+  int32_t kv_count;       // RANGED: number of keys; CELL_*: number of frames present
+  int32_t splits;         // RANGED: key-range splits per q tile (>= 1)
+  int32_t keys_per_split; // RANGED: keys per split, a multiple of KTILE
+  const void* k;          // K base of slot 0
+  const void* v;          // V base of slot 0
+  int64_t kv_sh, kv_st;   // slot (head) stride and token stride, elements
+  void* o;                // output base for this category
+  int64_t o_sh, o_st;     // output head / token strides, elements
+  float* part;            // split partials: [tile_id][splits][QTILE][D] fp32, then m,l
+  int32_t* counters;      // one per (head slot, q tile) when splits > 1
+  int32_t out_f32;        // output written as fp32 (else the input dtype)
+  int32_t pad_;
+};
+
+struct AttnPlan {
+  int32_t n_cats;
+  int32_t total_units;
+  int32_t q_tiles;         // ceil(Nq / QTILE), for ranged categories
+  int32_t cell_subtiles;   // q sub-tiles per spatial cell
+  // Q
+  const void* q;
+  int64_t q_sh, q_st;
+  // geometry
+  int32_t T, grid_w, grid_h, cell_h, cell_w, cell_cols, B, W, Nq;
+  float scale_log2;        // softmax scale * log2(e)
+  AttnCat cat[4];
+  uint8_t head_of[4][HC_MAX_HEADS];  // category slot -> q/o head index
+};
+
+// Launchers (return hipSuccess or the launch error).
+hipError_t launch_attn_bf16(const AttnPlan& plan, int head_dim, hipStream_t s);
+hipError_t launch_attn_f32(const AttnPlan& plan, int head_dim, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// Cache append.
+// ---------------------------------------------------------------------------
+struct AppendPlan {
+  const uint8_t* k;       // source block K (bytes), head / token strides in bytes
+  const uint8_t* v;
+  int64_t src_sh, src_st;
+  int32_t row_bytes;      // head_dim * element size
+  int32_t rows;           // B*T
+  int32_t H;
+  int32_t T, grid_w, grid_h, cell_h, cell_w, cell_cols, B, W;
+  int32_t ring_slot;      // (block index) mod (W/B)
+  int32_t write_sink;     // block index == 0
+  uint8_t* dst_k[4];      // per-archetype K buffer base (bytes), by label
+  uint8_t* dst_v[4];
+  int64_t dst_slot_bytes[4];
+  uint8_t label[HC_MAX_HEADS];
+  uint8_t slot[HC_MAX_HEADS];
+};
+hipError_t launch_append(const AppendPlan& plan, hipStream_t s);
+hipError_t launch_fill_zero(int32_t* p, int64_t n, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// Classifier reductions.
+// ---------------------------------------------------------------------------
+struct CosPlan {
+  const float* o;          // [4][H][Nq][D] fp32
+  float* c;                // [H][4][Nq]
+  int32_t H, Nq, D;
+};
+hipError_t launch_cosines(const CosPlan& plan, hipStream_t s);
+
+struct ReducePlan {
+  const float* c;          // [H][4][Nq]
+  int8_t* labels;          // [H]
+  float* diag;             // [H][4]
+  int32_t H, Nq, D;
+  float theta_sink, theta_dummy, theta_spatial, theta_score, gamma, percentile;
+  int32_t rule;
+};
+hipError_t launch_classify_reduce(const ReducePlan& plan, hipStream_t s);
+
+}  // namespace hc

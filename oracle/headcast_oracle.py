@@ -131,14 +131,15 @@ def default_scale(d: int) -> float:
 # Key sets: two independent formulations (a boolean mask over the window, and
 # an explicit per-query key list), so each checks the other.
 # ----------------------------------------------------------------------------
-def key_mask(geom: Geometry, pathway: int, n_frames: int | None = None, radius: int = 2):
+def key_mask(geom: Geometry, pathway: int, n_frames: int | None = None, radius: int = 2, rows=None):
     """Boolean [Nq, n_frames*T]: may query i attend to window key j?
+    With `rows`, only those query rows (in that order).
 
     Queries are the last block of the window: query i sits in window frame
     n_frames - B + i // T at the same (y, x) split as a key."""
     nf = geom.window_frames if n_frames is None else n_frames
     B, T = geom.block_frames, geom.T
-    qi = np.arange(B * T)
+    qi = np.arange(B * T) if rows is None else np.asarray(rows)
     kj = np.arange(nf * T)
     _, qy, qx = geom.split_token(qi)
     kf, ky, kx = geom.split_token(kj)
@@ -185,7 +186,8 @@ def key_list(geom: Geometry, pathway: int, i: int, n_frames: int | None = None, 
 def attention_masked(q, k, v, mask, scale: float, rows=None):
     """fp64 masked softmax attention for one head.
 
-    q [Nq, d], k [Nk, d], v [Nk, dv], mask [Nq, Nk] bool.  Returns [len(rows), dv].
+    q [Nq, d], k [Nk, d], v [Nk, dv]; mask is a bool [Nq, Nk] array or a
+    function rows -> bool [len(rows), Nk].  Returns [len(rows), dv].
     Each row must have at least one allowed key."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -195,7 +197,7 @@ def attention_masked(q, k, v, mask, scale: float, rows=None):
     for s in range(0, rows.size, QUERY_CHUNK):
         r = rows[s:s + QUERY_CHUNK]
         logits = scale * (q[r] @ k.T)
-        m = mask[r]
+        m = mask(r) if callable(mask) else mask[r]
         logits = np.where(m, logits, -np.inf)
         mx = logits.max(axis=1, keepdims=True)
         p = np.exp(logits - mx)           # exp(-inf) = 0 for masked keys
@@ -222,7 +224,7 @@ def attend_head(q, k, v, pathway: int, geom: Geometry, scale: float | None = Non
     """One head's output for one pathway over a frame-major window k/v."""
     scale = default_scale(q.shape[1]) if scale is None else scale
     nf = k.shape[0] // geom.T if n_frames is None else n_frames
-    mask = key_mask(geom, pathway, nf, radius)
+    mask = lambda r: key_mask(geom, pathway, nf, radius, rows=r)   # built chunk by chunk
     return attention_masked(q, k, v, mask, scale, rows)
 
 

@@ -1,0 +1,153 @@
+"""C ABI tests that need no GPU: the library loads, exports every function
+declared in include/headcast.h, and rejects bad arguments before any launch
+(host-only paths; device pointers here are never dereferenced)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from head_routed_kv_amd import _native as N
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "headcast.h")
+FAKE = 1 << 40          # 256-byte aligned, never dereferenced
+
+
+def declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(hc_[a-z_]+)\s*\(", src)))
+
+
+def cfg(**kw):
+    base = dict(num_heads=4, head_dim=128, grid_h=8, grid_w=12, block_frames=1, window_frames=4, cell_h=10,
+                cell_w=10, dtype=N.HC_BF16, softmax_scale=0.0)
+    base.update(kw)
+    return N.hc_config(**base)
+
+
+def status(fn, *args):
+    return fn(*args)
+
+
+def test_every_declared_symbol_is_exported():
+    L = N.lib()
+    names = declared()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(N.EXPORTS)
+
+
+def test_status_strings():
+    L = N.lib()
+    for s, name in [(0, b"HC_OK"), (-1, b"HC_ERR_INVALID_ARG"), (-6, b"HC_ERR_STATE"), (-8, b"HC_ERR_UNSUPPORTED")]:
+        assert L.hc_status_string(s) == name
+
+
+@pytest.mark.parametrize("kw,err", [
+    (dict(dtype=7), N.HC_ERR_DTYPE),
+    (dict(num_heads=0), N.HC_ERR_SHAPE),
+    (dict(num_heads=129), N.HC_ERR_SHAPE),
+    (dict(head_dim=96), N.HC_ERR_SHAPE),
+    (dict(window_frames=5, block_frames=2), N.HC_ERR_SHAPE),
+    (dict(grid_h=0), N.HC_ERR_SHAPE),
+    (dict(cell_w=0), N.HC_ERR_SHAPE),
+    (dict(softmax_scale=-1.0), N.HC_ERR_INVALID_ARG),
+])
+def test_bad_configs(kw, err):
+    c = cfg(**kw)
+    assert N.lib().hc_validate_config(C.byref(c)) == err
+    assert N.hc_last_error_message()
+
+
+def test_cache_bytes_and_layout():
+    c = cfg()
+    labels = [3, 2, 0, 1]
+    n = N.hc_cache_bytes(c, labels)
+    T, d = 96, 128
+    assert n >= 2 * 2 * (2 * 4 * T * d) + 2 * 2 * (2 * T * d)
+    h = N.hc_cache_create(c, labels, FAKE, n)
+    lay = N.hc_cache_get_layout(h)
+    assert lay.total_bytes == n
+    assert (lay.n_global, lay.n_sink, lay.n_dummy, lay.n_spatial) == (1, 1, 1, 1)
+    offs = [lay.off_global_k, lay.off_global_v, lay.off_sink_k, lay.off_sink_v, lay.off_dummy_k, lay.off_dummy_v,
+            lay.off_spatial_k, lay.off_spatial_v]
+    assert all(o % 256 == 0 for o in offs)
+    assert lay.off_global_v - lay.off_global_k >= 4 * T * d * 2
+    assert lay.blocks_appended == 0
+    N.hc_cache_destroy(h)
+
+
+def test_cache_create_errors():
+    c = cfg()
+    L = N.lib()
+    labs = (C.c_int8 * 4)(3, 2, 0, 1)
+    out = C.c_void_p()
+    n = N.hc_cache_bytes(c, [3, 2, 0, 1])
+    assert L.hc_cache_create(C.byref(c), labs, C.c_void_p(FAKE + 16), n, C.byref(out)) == N.HC_ERR_ALIGN
+    assert L.hc_cache_create(C.byref(c), labs, C.c_void_p(FAKE), n - 1, C.byref(out)) == N.HC_ERR_WORKSPACE
+    assert L.hc_cache_create(C.byref(c), labs, None, n, C.byref(out)) == N.HC_ERR_INVALID_ARG
+    bad = (C.c_int8 * 4)(3, 2, 4, 1)
+    assert L.hc_cache_create(C.byref(c), bad, C.c_void_p(FAKE), n, C.byref(out)) == N.HC_ERR_INVALID_ARG
+    assert "label" in N.hc_last_error_message()
+    assert L.hc_cache_bytes(C.byref(c), None, C.byref(C.c_size_t())) == N.HC_ERR_INVALID_ARG
+
+
+def test_misuse_is_rejected_before_launch():
+    c = cfg()
+    n = N.hc_cache_bytes(c, [3, 2, 0, 1])
+    h = N.hc_cache_create(c, [3, 2, 0, 1], FAKE, n)
+    L = N.lib()
+    q = N.hc_tensor(FAKE, 96 * 128, 128)
+    o = N.hc_out_tensor(FAKE + (1 << 30), 96 * 128, 128)
+    assert L.hc_attend(h, q, o, None) == N.HC_ERR_STATE                 # nothing appended yet
+    kv = N.hc_tensor(FAKE, 96 * 128, 128)
+    assert L.hc_cache_append(h, kv, kv, N.HC_REPLACE_NEWEST, None) == N.HC_ERR_STATE
+    assert L.hc_cache_append(h, kv, kv, 5, None) == N.HC_ERR_INVALID_ARG
+    assert L.hc_cache_append(h, N.hc_tensor(FAKE + 8, 96 * 128, 128), kv, 0, None) == N.HC_ERR_ALIGN
+    assert L.hc_cache_append(h, N.hc_tensor(FAKE, 96 * 128, 100), kv, 0, None) == N.HC_ERR_SHAPE
+    assert L.hc_cache_append(h, N.hc_tensor(None, 96 * 128, 128), kv, 0, None) == N.HC_ERR_INVALID_ARG
+    assert L.hc_cache_append(h, N.hc_tensor(FAKE, 96 * 128 + 4, 128), kv, 0, None) == N.HC_ERR_ALIGN
+    assert L.hc_attend(h, q, N.hc_out_tensor(FAKE, 96 * 128, 128), None) == N.HC_ERR_INVALID_ARG  # aliases q
+    N.hc_cache_destroy(h)
+    assert L.hc_cache_destroy(None) == N.HC_ERR_INVALID_ARG
+
+
+def test_classify_argument_checks():
+    c = cfg()
+    L = N.lib()
+    p = N.hc_default_classify_params()
+    assert (round(p.theta_sink, 6), round(p.theta_score, 6), p.gamma, p.percentile, p.rule, p.radius) == \
+        (0.95, 0.755, 5.0, 5.0, 0, 2)
+    need = N.hc_classify_workspace_bytes(c)
+    assert need >= 4 * 4 * 96 * 128 * 4
+    t = N.hc_tensor(FAKE, 384 * 128, 128)
+    args = lambda prm, ws, wsb: (C.byref(c), C.byref(prm), t, t, t, C.c_void_p(ws), wsb, C.c_void_p(FAKE),
+                                 C.c_void_p(FAKE), None)
+    assert L.hc_classify(*args(p, FAKE, need - 1)) == N.HC_ERR_WORKSPACE
+    assert L.hc_classify(*args(p, FAKE + 16, need)) == N.HC_ERR_ALIGN
+    p2 = N.hc_default_classify_params()
+    p2.spatial_proxy = 1
+    assert L.hc_classify(*args(p2, FAKE, need)) == N.HC_ERR_UNSUPPORTED
+    p3 = N.hc_default_classify_params()
+    p3.rule = 3
+    assert L.hc_classify(*args(p3, FAKE, need)) == N.HC_ERR_INVALID_ARG
+    p4 = N.hc_default_classify_params()
+    p4.percentile = 101
+    assert L.hc_classify(*args(p4, FAKE, need)) == N.HC_ERR_INVALID_ARG
+
+
+def test_split_plan_for_benchmark_layers():
+    """The host plans key-range splits for Global heads when their q tiles
+    alone cannot fill the chip (720p: 3 Global heads x 85 q tiles)."""
+    c = N.make_config(12, 128, 45, 80, 3, 21)
+    labels = [2, 0, 3, 1, 3, 2, 2, 3, 2, 2, 0, 1]
+    h = N.hc_cache_create(c, labels, FAKE, N.hc_cache_bytes(c, labels))
+    lay = N.hc_cache_get_layout(h)
+    assert lay.global_splits > 1 and lay.scratch_bytes > 0
+    N.hc_cache_destroy(h)
+    h = N.hc_cache_create(cfg(), [0, 1, 2, 3], FAKE, N.hc_cache_bytes(cfg(), [0, 1, 2, 3]))
+    assert N.hc_cache_get_layout(h).global_splits == 1
+    N.hc_cache_destroy(h)

@@ -1,0 +1,199 @@
+"""GPU parity of the restructured cache and routed attention (hc_cache_append,
+hc_attend) against the CPU oracle."""
+import numpy as np
+import pytest
+
+import head_routed_kv_amd as hk
+from head_routed_kv_amd import workloads as W
+from oracle import headcast_oracle as O
+from tests.gpu_util import (BF16_TOL, FP32_TOL, check_close, config_of, download_bits, fill_cache, geometry_of,
+                            sample_rows, say, to_float, torch, upload)
+
+pytestmark = pytest.mark.gpu
+
+
+def run_window(wl, labels, seed=0):
+    data = W.window(wl, seed=seed)
+    q, k, v = (upload(data[n], wl) for n in ("q", "k", "v"))
+    cache = fill_cache(wl, labels, k, v)
+    out = cache.attend(q)
+    torch().cuda.synchronize()
+    return data, cache, out
+
+
+def oracle_routed(wl, data, labels, rows=None):
+    fq, fk, fv = (W.as_float(data[n], wl) for n in ("q", "k", "v"))
+    return O.routed_attention(fq, fk, fv, np.asarray(labels), geometry_of(wl), rows=rows)
+
+
+def test_tiny_fp32_routed():
+    wl = W.WORKLOADS["tiny"]
+    labels = W.make_labels(wl)
+    say("case tiny fp32", labels)
+    data, cache, out = run_window(wl, labels)
+    check_close(to_float(out), oracle_routed(wl, data, labels), FP32_TOL, "tiny")
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_small_bf16_every_pathway(d):
+    """Several q tiles and key tiles with ragged tails, uneven border cells."""
+    wl = W.Workload("small", 9, 8, d, 23, 37, 2, 6, "bf16", "uniform")
+    labels = [0, 1, 2, 3, 3, 2, 1, 0]
+    say("case small bf16 d", d)
+    data, cache, out = run_window(wl, labels, seed=5)
+    assert cache.layout().global_splits >= 1
+    check_close(to_float(out), oracle_routed(wl, data, labels), BF16_TOL, f"small d{d}")
+
+
+def test_global_key_splits_merge():
+    """Few queries over a long window: the cache plans several key-range
+    splits for the Global head and merges them in the kernel."""
+    wl = W.Workload("longwin", 10, 3, 128, 16, 16, 1, 64, "bf16", "uniform")
+    labels = [3, 0, 3]
+    say("case long window split merge")
+    data, cache, out = run_window(wl, labels, seed=6)
+    assert cache.layout().global_splits > 1
+    check_close(to_float(out), oracle_routed(wl, data, labels), BF16_TOL, "split")
+    # a second call reuses the self-resetting counters
+    out2 = cache.attend(upload(data["q"], wl))
+    torch().cuda.synchronize()
+    assert torch().equal(out, out2)
+
+
+def test_fp32_spatial_and_global_small():
+    wl = W.Workload("small32", 11, 4, 128, 13, 21, 2, 6, "fp32", "uniform")
+    labels = [2, 3, 1, 0]
+    say("case small fp32 d128")
+    data, cache, out = run_window(wl, labels, seed=7)
+    check_close(to_float(out), oracle_routed(wl, data, labels), FP32_TOL, "small fp32")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_streaming_wrap_replace(dtype):
+    """Push past the window (ring wrap), replace the newest block, attend after
+    each step; the sink block stays the video's first block."""
+    wl = W.Workload("stream", 12, 4, 64, 12, 17, 1, 3, dtype, "uniform")
+    labels = [0, 1, 2, 3]
+    g = geometry_of(wl)
+    cache = hk.RoutedCache(config_of(wl), labels)
+    model = O.CacheModel(g, labels)
+    ks, vs = W.stream_blocks(wl, 8, 9)
+    ks2, vs2 = W.stream_blocks(wl, 9, 9)
+    q = W.queries(wl, 8)
+    qd = upload(q, wl)
+    for step in range(9):
+        mode = hk.HC_REPLACE_NEWEST if step in (2, 6) else hk.HC_PUSH_BLOCK
+        kb, vb = (ks2[step], vs2[step]) if mode == hk.HC_REPLACE_NEWEST else (ks[step], vs[step])
+        cache.append(upload(kb, wl), upload(vb, wl), mode)
+        model.append(kb, vb, mode)
+        out = cache.attend(qd)
+        torch().cuda.synchronize()
+        wk, wv = model.window()
+        nf = wk.shape[1] // g.T
+        gq = O.Geometry(g.grid_h, g.grid_w, g.block_frames, nf, g.cell_h, g.cell_w)
+        ref = O.routed_attention(W.as_float(q, wl), W.as_float(wk, wl), W.as_float(wv, wl), np.array(labels), gq,
+                                 k_sink=W.as_float(model.sink_k, wl), v_sink=W.as_float(model.sink_v, wl))
+        check_close(to_float(out), ref, BF16_TOL if dtype == "bf16" else FP32_TOL, f"step {step}")
+
+
+def test_cache_buffers_bit_exact():
+    """Every archetype buffer equals the oracle's index model byte for byte."""
+    wl = W.Workload("bits", 13, 6, 64, 13, 23, 2, 6, "bf16", "uniform")
+    labels = [2, 3, 0, 1, 3, 2]
+    g = geometry_of(wl)
+    cache = hk.RoutedCache(config_of(wl), labels)
+    model = O.CacheModel(g, labels)
+    ks, vs = W.stream_blocks(wl, 4, 6)
+    ks2, vs2 = W.stream_blocks(wl, 5, 6)
+    mem = cache.mem
+    for step in range(6):
+        mode = hk.HC_REPLACE_NEWEST if step == 4 else hk.HC_PUSH_BLOCK
+        kb, vb = (ks2[step], vs2[step]) if mode else (ks[step], vs[step])
+        cache.append(upload(kb, wl), upload(vb, wl), mode)
+        model.append(kb, vb, mode)
+        torch().cuda.synchronize()
+        lay = cache.layout()
+        raw = mem.cpu().numpy()
+        for lab, (ok, ov) in {O.GLOBAL: (lay.off_global_k, lay.off_global_v),
+                              O.SINK: (lay.off_sink_k, lay.off_sink_v),
+                              O.DUMMY: (lay.off_dummy_k, lay.off_dummy_v),
+                              O.SPATIAL: (lay.off_spatial_k, lay.off_spatial_v)}.items():
+            for which, off in (("k", ok), ("v", ov)):
+                exp, valid = model.expected_buffer(lab, which)
+                n = exp.size * 2
+                got = raw[off:off + n].view(np.uint16).reshape(exp.shape)
+                assert np.array_equal(got[:, valid], exp[:, valid]), (step, lab, which)
+        for h, lab in enumerate(labels):
+            assert lay.head_slot[h] == sum(1 for x in labels[:h] if x == lab)
+
+
+def test_strided_token_major_inputs():
+    """[tokens][heads][d] views give bit-identical results to [heads][tokens][d]."""
+    wl = W.Workload("strided", 14, 4, 128, 11, 19, 2, 4, "bf16", "uniform")
+    labels = [3, 2, 1, 0]
+    data = W.window(wl, seed=9)
+    q, k, v = (upload(data[n], wl) for n in ("q", "k", "v"))
+    ref_cache = fill_cache(wl, labels, k, v)
+    ref = ref_cache.attend(q)
+    tq, tk, tv = (x.transpose(0, 1).contiguous().transpose(0, 1) for x in (q, k, v))
+    assert tq.stride(1) == wl.heads * wl.head_dim
+    cache = fill_cache(wl, labels, tk, tv)
+    out = torch().empty(wl.Nq, wl.heads, wl.head_dim, dtype=q.dtype, device=q.device).transpose(0, 1)
+    cache.attend(tq, out)
+    torch().cuda.synchronize()
+    assert torch().equal(out, ref)
+
+
+FULL = ["480p", "720p", "1080p"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled_rows(name):
+    """Full-size layer in the launch configuration the benchmark times,
+    checked on sampled query rows (oracle row by row)."""
+    wl = W.WORKLOADS[name]
+    labels = W.make_labels(wl)
+    say("case", name, "labels", labels.tolist())
+    data, cache, out = run_window(wl, labels)
+    rows = sample_rows(wl, 40 if name == "1080p" else 64)
+    got = to_float(out)[:, rows]
+    heads = range(wl.heads) if name != "1080p" else sorted(set(np.random.default_rng(1).choice(40, 12, False)))
+    heads = list(heads)
+    fq, fk, fv = (W.as_float(data[n], wl) for n in ("q", "k", "v"))
+    g = geometry_of(wl)
+    ref = np.stack([O.attend_head(fq[h], fk[h], fv[h], int(labels[h]), g, rows=rows) for h in heads])
+    worst = check_close(got[heads], ref, BF16_TOL, name)
+    say(name, "worst err/rms", worst, "splits", cache.layout().global_splits)
+
+
+def test_full_attention_baseline_720p_sampled():
+    """All heads Global is the full-attention baseline the speedup is taken over."""
+    wl = W.WORKLOADS["720p"]
+    labels = np.full(wl.heads, O.GLOBAL)
+    data, cache, out = run_window(wl, labels)
+    rows = sample_rows(wl, 32, seed=3)
+    fq, fk, fv = (W.as_float(data[n], wl) for n in ("q", "k", "v"))
+    g = geometry_of(wl)
+    heads = [0, 5, 11]
+    ref = np.stack([O.attend_head(fq[h], fk[h], fv[h], O.GLOBAL, g, rows=rows) for h in heads])
+    check_close(to_float(out)[heads][:, rows], ref, BF16_TOL, "full-attention baseline")
+
+
+def test_spatial_cell_covering_frame_equals_global():
+    """A Spatial head whose cell covers the frame reads the whole window."""
+    wl = W.Workload("bigcell", 15, 2, 128, 9, 14, 1, 4, "bf16", "uniform", cell_h=9, cell_w=14)
+    data = W.window(wl, seed=10)
+    q, k, v = (upload(data[n], wl) for n in ("q", "k", "v"))
+    a = fill_cache(wl, [2, 2], k, v).attend(q)
+    b = fill_cache(wl, [3, 3], k, v).attend(q)
+    torch().cuda.synchronize()
+    check_close(to_float(a), to_float(b), BF16_TOL, "cell == frame")
+
+
+def test_repeat_calls_deterministic():
+    wl = W.Workload("det", 16, 6, 128, 20, 30, 3, 9, "bf16", "uniform")
+    labels = [3, 3, 2, 1, 0, 2]
+    data, cache, out = run_window(wl, labels, seed=12)
+    out2 = cache.attend(upload(data["q"], wl))
+    torch().cuda.synchronize()
+    assert np.array_equal(download_bits(out), download_bits(out2))

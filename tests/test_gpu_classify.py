@@ -1,0 +1,95 @@
+"""GPU parity of the one-shot classifier (hc_classify) against the CPU oracle:
+the four outputs, per-query cosines, per-head diagnostics and labels."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import head_routed_kv_amd as hk
+from head_routed_kv_amd import workloads as W
+from oracle import headcast_oracle as O
+from tests.gpu_util import BF16_TOL, FP32_TOL, check_close, config_of, geometry_of, say, torch, upload
+
+pytestmark = pytest.mark.gpu
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def run_classify(wl, data, params=None):
+    cfg = config_of(wl)
+    q, k, v = (upload(data[n], wl) for n in ("q", "k", "v"))
+    labels, diag, ws = hk.classify(cfg, q, k, v, params)
+    torch().cuda.synchronize()
+    H, Nq, d = wl.heads, wl.Nq, wl.head_dim
+    outs = ws[:4 * H * Nq * d * 4].view(torch().float32).view(4, H, Nq, d)
+    off = ((4 * H * Nq * d * 4 + 255) // 256) * 256
+    cos = ws[off:off + H * 4 * Nq * 4].view(torch().float32).view(H, 4, Nq)
+    return labels.cpu().numpy(), diag.cpu().numpy(), outs, cos
+
+
+def oracle_head(wl, data, h, params=O.ClassifyParams()):
+    fq, fk, fv = (W.as_float(data[n], wl)[h] for n in ("q", "k", "v"))
+    g = geometry_of(wl)
+    outs = [O.attend_head(fq, fk, fv, p, g) for p in (O.GLOBAL, O.SINK, O.DUMMY, O.SPATIAL)]
+    diag, cos, mse = O.head_scores(*outs, params)
+    return outs, diag, cos, mse, O.decide_label(diag, params), O.decision_margin(diag, params)
+
+
+@pytest.mark.parametrize("name,tol,dtol", [("tiny", FP32_TOL, 1e-5), ("planted-small", BF16_TOL, 1e-2)])
+def test_classifier_small_full_compare(name, tol, dtol):
+    if name == "tiny":
+        wl = W.WORKLOADS["tiny"]
+        data = W.window(wl, seed=0)
+    else:
+        wl = W.small(W.WORKLOADS["classifier720p"], grid_h=20, grid_w=30, heads=12, window_frames=9)
+        data = W.window(wl, seed=2)
+    say("case classify", name)
+    labels, diag, outs, cos = run_classify(wl, data)
+    for h in range(wl.heads):
+        o_outs, o_diag, o_cos, o_mse, o_lab, margin = oracle_head(wl, data, h)
+        for p in range(4):
+            check_close(outs[p, h].cpu().numpy()[None], o_outs[p][None], tol, f"{name} head {h} output {p}")
+        np.testing.assert_allclose(cos[h, :3].cpu().numpy(), o_cos, atol=dtol)
+        np.testing.assert_allclose(diag[h], o_diag, atol=dtol)
+        if margin > 10 * dtol:
+            assert labels[h] == o_lab, (h, labels[h], o_lab, o_diag)
+    if name == "planted-small":
+        np.testing.assert_array_equal(labels, data["labels"])
+
+
+def test_classifier_rule_variants_and_percentile():
+    """rule 1 and other percentile ranks on the same planted data."""
+    wl = W.small(W.WORKLOADS["classifier720p"], grid_h=20, grid_w=30, heads=12, window_frames=9)
+    data = W.window(wl, seed=2)
+    p = hk.hc_default_classify_params()
+    p.rule = 1
+    p.percentile = 37.5
+    p.theta_sink = 0.3          # lets several proxies clear, so the two rules differ
+    op = O.ClassifyParams(rule=1, percentile=37.5, theta_sink=0.3)
+    labels, diag, _, _ = run_classify(wl, data, p)
+    for h in range(wl.heads):
+        _, o_diag, _, _, o_lab, margin = oracle_head(wl, data, h, op)
+        np.testing.assert_allclose(diag[h], o_diag, atol=1e-2)
+        if margin > 0.05:
+            assert labels[h] == o_lab
+
+
+def test_classifier_720p_planted_golden():
+    """40 planted heads at the 720p shape: labels bit-exact against the
+    oracle's stored result, diagnostics within tolerance."""
+    path = os.path.join(GOLDEN, "classifier720p_seed0.json")
+    gold = json.load(open(path))
+    wl = W.WORKLOADS["classifier720p"]
+    data = W.window(wl, seed=0)
+    say("case classify 720p planted")
+    labels, diag, outs, cos = run_classify(wl, data)
+    assert min(gold["margin"]) > 1e-2
+    np.testing.assert_array_equal(labels, np.array(gold["labels"], dtype=np.int8))
+    np.testing.assert_allclose(diag, np.array(gold["diag"]), atol=1e-2)
+    # spot-check the full-context output rows of two heads
+    rows = np.array([0, 5000, 10799])
+    g = geometry_of(wl)
+    for h in (0, 17):
+        fq, fk, fv = (W.as_float(data[n], wl)[h] for n in ("q", "k", "v"))
+        ref = O.attend_head(fq, fk, fv, O.GLOBAL, g, rows=rows)
+        check_close(outs[0, h].cpu().numpy()[rows][None], ref[None], BF16_TOL, f"720p full output head {h}")

@@ -72,6 +72,13 @@ def test_keyset_mask_equals_keylist(pathway, geom):
         assert np.array_equal(np.flatnonzero(mask[i]), np.sort(O.key_list(geom, pathway, i))), i
 
 
+def test_keyset_mask_rows_subset():
+    g = O.Geometry(13, 23, 2, 6)
+    rows = np.array([5, 0, 597, 300, 1])
+    for p in (O.SINK, O.DUMMY, O.SPATIAL, O.GLOBAL, O.SLIDING):
+        assert np.array_equal(O.key_mask(g, p, rows=rows), O.key_mask(g, p)[rows])
+
+
 def test_keyset_brute_force_tiny():
     """Brute force over (frame, y, x) on the tiny grid, straight from the
     archetype descriptions."""
