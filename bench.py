@@ -153,6 +153,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the 1080p and per-pathway figures")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="also run a plain 1 GiB device copy (known bytes) to scale HBM counters")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {a.gpus}). "
@@ -164,6 +166,13 @@ def main():
     from head_routed_kv_amd import workloads as W
 
     dev = torch.device("cuda:0")
+    if a.calibrate:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)     # reads 1 GiB, writes 1 GiB
+        torch.cuda.synchronize()
+        del src, dst
     wl = W.WORKLOADS[a.workload]
     labels = W.make_labels(wl, a.seed)
     q, k, v = gen_inputs(wl, a.seed, dev)

@@ -512,7 +512,22 @@ hc_status hc_classify(const hc_config* cfg, const hc_classify_params* prm, hc_te
   }
   P.n_cats = 4;
   P.total_units = units;
-  hipError_t err = cfg->dtype == HC_BF16 ? launch_attn_bf16(P, D, stream) : launch_attn_f32(P, D, stream);
+  hipError_t err;
+  if (cfg->dtype == HC_BF16) {
+    // the matrix-core kernel is specialised on gathered keys: full / sink /
+    // dummy (contiguous key ranges) in one launch, the Spatial proxy in another
+    AttnPlan G = P;
+    P.n_cats = 3;
+    P.total_units = P.cat[3].unit_begin;
+    G.cat[0] = G.cat[3];
+    G.cat[0].unit_begin = 0;
+    G.n_cats = 1;
+    G.total_units = H * G.cat[0].units_per_head;
+    err = launch_attn_bf16(P, D, stream);
+    if (err == hipSuccess) err = launch_attn_bf16(G, D, stream);
+  } else {
+    err = launch_attn_f32(P, D, stream);
+  }
   if (err != hipSuccess) return hip_fail(err, "classifier attention launch");
 
   CosPlan cp{O, Cc, H, g.Nq, D};

@@ -74,11 +74,21 @@ __device__ __forceinline__ int cell_token(const AttnPlan& P, const CellInfo& c, 
   return f * P.T + c.base + ry * P.grid_w + (r - ry * c.width);
 }
 
-__device__ __forceinline__ float wave_xor32(float x) {
-  return __shfl_xor(x, 32, 64);
+// Values of lanes l and l^32 (in either order), via v_permlane32_swap.
+struct Pair {
+  float a, b;
+};
+__device__ __forceinline__ Pair halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return Pair{__uint_as_float(r[0]), __uint_as_float(r[1])};
 }
 
-template <int D, bool OUT_F32>
+// Lazy rescaling: the running max is only raised when a tile's max exceeds it
+// by more than 2^8 in probability, so exp2 arguments stay <= 8 and the O
+// accumulator is rescaled on a few early tiles only.
+constexpr float kLazyLog2 = 8.0f;
+
+template <int D, bool OUT_F32, bool GATHER>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(const AttnPlan P) {
   using TL = Tile<D>;
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * TL::BUF];
@@ -121,7 +131,6 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     kn = C.kv_count * cell.size;          // frames present x |c|
     k0 = (C.kind == KIND_CELL_MAJOR) ? P.W * cell.off : 0;
   }
-  const bool gather = (C.kind == KIND_CELL_GATHER);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -152,25 +161,48 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   const int vo = tid / 16, va = tid % 16;                   // V: channels 8*vo.., keys 4*va..
   const bool vtask = tid < TL::VTASKS;
 
-  auto key_row = [&](int kk) -> int64_t {   // kk: index into this unit's key list
-    if (!gather) return (int64_t)(k0 + kk) * C.kv_st;
-    return (int64_t)cell_token(P, cell, kk) * C.kv_st;
-  };
+  // Contiguous key rows: a uniform (scalar) tile base plus a per-thread
+  // 32-bit byte offset; only the ragged last tile checks rows.
+  const int64_t rowb = C.kv_st * 2;                       // bytes per key row
+  const uint32_t vko = (uint32_t)(kr0 * rowb + 16 * kch);
+  const uint32_t vvo = (uint32_t)(4 * va * rowb + 16 * vo);
+  const char* __restrict__ Kc = (const char*)Kb;
+  const char* __restrict__ Vc = (const char*)Vb;
 
   u32x4 kreg[TL::KPASS];
   u32x4 vreg[4];
   auto load_tile = [&](int kb) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    if constexpr (!GATHER) {
+      const char* kt = Kc + (int64_t)(k0 + kb) * rowb;
+      const char* vt = Vc + (int64_t)(k0 + kb) * rowb;
+      if (kb + KTILE <= kn) {
 #pragma unroll
-    for (int i = 0; i < TL::KPASS; ++i) {
-      const int kk = kb + kr0 + TL::RPP * i;
-      kreg[i] = u32x4{0u, 0u, 0u, 0u};
-      if (kk < kn) kreg[i] = *(const u32x4*)(Kb + key_row(kk) + 8 * kch);
-    }
+        for (int i = 0; i < TL::KPASS; ++i) kreg[i] = *(const u32x4*)(kt + i * TL::RPP * rowb + vko);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int kk = kb + 4 * va + r;
-      vreg[r] = u32x4{0u, 0u, 0u, 0u};
-      if (vtask && kk < kn) vreg[r] = *(const u32x4*)(Vb + key_row(kk) + 8 * vo);
+        for (int r = 0; r < 4; ++r)
+          vreg[r] = (TL::VTASKS == NT || vtask) ? *(const u32x4*)(vt + r * rowb + vvo) : z;
+      } else {
+#pragma unroll
+        for (int i = 0; i < TL::KPASS; ++i)
+          kreg[i] = (kb + kr0 + TL::RPP * i < kn) ? *(const u32x4*)(kt + i * TL::RPP * rowb + vko) : z;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          vreg[r] = (vtask && kb + 4 * va + r < kn) ? *(const u32x4*)(vt + r * rowb + vvo) : z;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < TL::KPASS; ++i) {
+        const int kk = kb + kr0 + TL::RPP * i;
+        kreg[i] = z;
+        if (kk < kn) kreg[i] = *(const u32x4*)(Kb + (int64_t)cell_token(P, cell, kk) * C.kv_st + 8 * kch);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int kk = kb + 4 * va + r;
+        vreg[r] = z;
+        if (vtask && kk < kn) vreg[r] = *(const u32x4*)(Vb + (int64_t)cell_token(P, cell, kk) * C.kv_st + 8 * vo);
+      }
     }
   };
   auto store_tile = [&](int buf) {
@@ -241,10 +273,20 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       for (int jj = 1; jj < 16; ++jj) mx = fmaxf(mx, s0[jj]);
 #pragma unroll
       for (int jj = 0; jj < 16; ++jj) mx = fmaxf(mx, s1[jj]);
-      mx = fmaxf(mx, wave_xor32(mx));
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c2);
-      const float mc = m_new * c2;
+      {
+        const Pair pr = halves(mx);
+        mx = fmaxf(pr.a, pr.b);
+      }
+      const bool grow = mx * c2 > fmaf(m_run, c2, kLazyLog2);
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {   // wave-uniform
+        const float m_new = grow ? mx : m_run;
+        const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c2);
+        l_run *= alpha;
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t) oacc[t] *= alpha;
+        m_run = m_new;
+      }
+      const float mc = m_run * c2;
       float psum = 0.f;
 #pragma unroll
       for (int jj = 0; jj < 16; ++jj) {
@@ -252,10 +294,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         s1[jj] = __builtin_amdgcn_exp2f(fmaf(s1[jj], c2, -mc));
         psum += s0[jj] + s1[jj];
       }
-      l_run = fmaf(l_run, alpha, psum);
-      m_run = m_new;
-#pragma unroll
-      for (int t = 0; t < D / 32; ++t) oacc[t] *= alpha;
+      l_run += psum;
 
       bf16x8 pb[4];
 #pragma unroll
@@ -279,7 +318,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   }
 
   // ---- epilogue -------------------------------------------------------------
-  const float l_tot = l_run + wave_xor32(l_run);
+  float l_tot;
+  {
+    const Pair pr = halves(l_run);
+    l_tot = pr.a + pr.b;
+  }
   const int splits = ranged ? C.splits : 1;
 
   if (splits > 1) {
@@ -379,15 +422,20 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 
 hipError_t launch_attn_bf16(const AttnPlan& plan, int head_dim, hipStream_t s) {
   if (plan.total_units <= 0) return hipSuccess;
-  bool f32 = plan.cat[0].out_f32 != 0;
+  const bool f32 = plan.cat[0].out_f32 != 0;
+  const bool gather = plan.cat[0].kind == KIND_CELL_GATHER;
+  for (int c = 1; c < plan.n_cats; ++c)
+    if ((plan.cat[c].kind == KIND_CELL_GATHER) != gather) return hipErrorInvalidValue;  // one mode per launch
   dim3 grid(plan.total_units), block(NT);
+#define HC_LAUNCH(DD, F, G) hipLaunchKernelGGL((attn_bf16_kernel<DD, F, G>), grid, block, 0, s, plan)
   if (head_dim == 128) {
-    if (f32) hipLaunchKernelGGL((attn_bf16_kernel<128, true>), grid, block, 0, s, plan);
-    else hipLaunchKernelGGL((attn_bf16_kernel<128, false>), grid, block, 0, s, plan);
+    if (gather) { if (f32) HC_LAUNCH(128, true, true); else HC_LAUNCH(128, false, true); }
+    else { if (f32) HC_LAUNCH(128, true, false); else HC_LAUNCH(128, false, false); }
   } else {
-    if (f32) hipLaunchKernelGGL((attn_bf16_kernel<64, true>), grid, block, 0, s, plan);
-    else hipLaunchKernelGGL((attn_bf16_kernel<64, false>), grid, block, 0, s, plan);
+    if (gather) { if (f32) HC_LAUNCH(64, true, true); else HC_LAUNCH(64, false, true); }
+    else { if (f32) HC_LAUNCH(64, true, false); else HC_LAUNCH(64, false, false); }
   }
+#undef HC_LAUNCH
   return hipGetLastError();
 }
 

@@ -187,7 +187,9 @@ def test_spatial_cell_covering_frame_equals_global():
     a = fill_cache(wl, [2, 2], k, v).attend(q)
     b = fill_cache(wl, [3, 3], k, v).attend(q)
     torch().cuda.synchronize()
-    check_close(to_float(a), to_float(b), BF16_TOL, "cell == frame")
+    ref = oracle_routed(wl, data, [3, 3])     # the Global pathway = full attention
+    check_close(to_float(a), ref, BF16_TOL, "spatial, cell == frame")
+    check_close(to_float(b), ref, BF16_TOL, "global")
 
 
 def test_repeat_calls_deterministic():
