@@ -21,9 +21,13 @@ SOURCES = ["api.hip", "append.hip", "attn_bf16.hip", "attn_f32.hip", "classify.h
 ARCH = os.environ.get("HEADCAST_ARCH", "gfx950")
 
 # Packed fp32 VALU instructions stay off: the compiler otherwise forms them
-# from ordinary float code.
+# from ordinary float code.  MFMAs are selected in VGPR form: the attention
+# kernel's softmax reads the score accumulators with VALU instructions, and the
+# AGPR form made the register allocator copy every O accumulator between AGPRs
+# and VGPRs on each key tile.
 HIPCC_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+               "-mllvm", "-amdgpu-mfma-vgpr-form=1",
                "-I", os.path.join(ROOT, "include"), "-Wno-unused-result"]
 
 

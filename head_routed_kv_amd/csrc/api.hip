@@ -38,9 +38,9 @@ size_t elt_size(int dtype) { return dtype == HC_BF16 ? 2 : 4; }
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
-// The split plan is made for the 256 compute units of an MI355X, two work
-// groups of the attention kernel per compute unit.
-constexpr int kWorkGroupSlots = 256 * 2;
+// The split plan is made for the 256 compute units of an MI355X, one work
+// group of the bf16 attention kernel per compute unit.
+constexpr int kWorkGroupSlots = 256 * (kBf16QueryBlocks == 1 ? 2 : 1);
 constexpr int kMaxSplits = 8;
 
 hc_status check_config(const hc_config* c) {
@@ -83,8 +83,11 @@ struct Geom {
   std::vector<int> cell_size;
 };
 
+int qtile_of(const hc_config* c) { return c->dtype == HC_BF16 ? QTILE_BF16 : QTILE_F32; }
+
 Geom geometry(const hc_config* c) {
   Geom g;
+  const int QTILE = qtile_of(c);
   g.T = c->grid_h * c->grid_w;
   g.Nq = c->block_frames * g.T;
   g.Nk = c->window_frames * g.T;
@@ -127,7 +130,7 @@ double simulate(const hc_config* c, const Geom& g, const int count[4], int split
   for (int h = 0; h < count[HC_SPATIAL]; ++h)
     for (int cl = 0; cl < g.n_cells; ++cl) {
       const int qall = c->block_frames * g.cell_size[cl];
-      const int sub = cdiv(qall, QTILE);
+      const int sub = cdiv(qall, qtile_of(c));
       run(cdiv((int64_t)c->window_frames * g.cell_size[cl], KTILE) + fixed, sub);
     }
   double mk = 0;
@@ -188,7 +191,7 @@ hc_status make_layout(const hc_config* c, const int8_t* labels, Layout* L) {
   L->off_part = off;
   if (L->splits > 1) {
     const int64_t ids = (int64_t)L->count[HC_GLOBAL] * g.q_tiles;
-    const size_t part = (size_t)ids * L->splits * QTILE * ((size_t)c->head_dim + 2) * sizeof(float);
+    const size_t part = (size_t)ids * L->splits * qtile_of(c) * ((size_t)c->head_dim + 2) * sizeof(float);
     L->off_counters = align256(off + part);
     L->n_counters = ids;
     off = align256(L->off_counters + ids * sizeof(int32_t));

@@ -4,28 +4,31 @@
 // head's buffer, the Spatial pathway is exact attention over the keys of the
 // query's latent cell in every cached frame (HeadCast review page, "What
 // carries the argument" and Fig. 3: per-head pathways, non-overlapping grid
-// cells).  Each work group owns 128 queries (4 waves x 32) and streams the
-// key set in 64-key tiles through LDS with online softmax.
+// cells).
 //
-// Per wave and key tile:
-//   S^T (64 keys x 32 queries) = K_tile . Q^T      4 x v_mfma_f32_32x32x16_bf16 per 32 keys
-//   O^T (D x 32)             += V_tile^T . P^T     D/32 x 4 MFMAs
-// Computing S transposed puts one query per lane (32 scores per lane, the
-// other 32 of the tile in lane^32), so the row max needs one cross-lane
-// exchange and the rescale of O is a per-lane scalar.  V is transposed while
-// being staged into LDS, with bits 2 and 3 of the key index swapped so that
-// every MFMA operand read is one 16-byte LDS load.
+// A work group is 4 waves; each wave owns QB blocks of 32 queries, so a work
+// group owns 128*QB queries and streams the key set in 64-key tiles through
+// double-buffered LDS with online softmax.  Per wave and key tile:
+//   S^T (64 keys x 32 queries) = K_tile . Q^T      per query block: 2 x D/16 v_mfma_f32_32x32x16_bf16
+//   O^T (D x 32)             += V_tile^T . P^T     per query block: D/32 x 4 MFMAs
+// Every K and V^T operand read from LDS feeds all QB query blocks, so LDS
+// bytes per MFMA fall as 1/QB (the LDS read port, not the matrix core, bounds
+// a 32-query wave).  Computing S transposed puts one query per lane (32
+// scores per lane, the other 32 of the tile in lane^32), so the row max needs
+// one v_permlane32_swap and rescaling O is a per-lane scalar.  V is transposed
+// while being staged into LDS, with bits 2 and 3 of the key index swapped so
+// that every MFMA operand read is a single 16-byte LDS load.
 #include "hc_internal.h"
 
 namespace hc {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int NT = 256;  // threads per work group
 
@@ -88,9 +91,21 @@ __device__ __forceinline__ Pair halves(float x) {
 // accumulator is rescaled on a few early tiles only.
 constexpr float kLazyLog2 = 8.0f;
 
-template <int D, bool OUT_F32, bool GATHER>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(const AttnPlan P) {
+template <bool OUT_F32>
+__device__ __forceinline__ void store_row4(void* base, int64_t off, f32x4 v) {
+  if constexpr (OUT_F32) {
+    *(f32x4*)((float*)base + off) = v;
+  } else {
+    bf16x4 b = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+    *(u32x2*)((uint16_t*)base + off) = __builtin_bit_cast(u32x2, b);
+  }
+}
+
+template <int D, int QB, bool OUT_F32, bool GATHER>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(QB == 1 ? 2 : 1, QB == 1 ? 2 : 1)))
+void attn_bf16_kernel(const AttnPlan P) {
   using TL = Tile<D>;
+  constexpr int QT = 128 * QB;   // queries per work group
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * TL::BUF];
   __shared__ int s_last;
 
@@ -116,18 +131,18 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   if (ranged) {
     split = j / P.q_tiles;
     tile = j - split * P.q_tiles;
-    q0 = tile * QTILE;
-    qn = min(QTILE, P.Nq - q0);
+    q0 = tile * QT;
+    qn = min(QT, P.Nq - q0);
     k0 = C.kv_first + split * C.keys_per_split;
     kn = min(C.keys_per_split, C.kv_count - split * C.keys_per_split);
   } else {
     const int c = j / P.cell_subtiles;
     const int st = j - c * P.cell_subtiles;
     cell = cell_info(P, c);
-    q0 = st * QTILE;
+    q0 = st * QT;
     const int qall = P.B * cell.size;
     if (q0 >= qall) return;  // empty sub-tile of a small border cell
-    qn = min(QTILE, qall - q0);
+    qn = min(QT, qall - q0);
     kn = C.kv_count * cell.size;          // frames present x |c|
     k0 = (C.kind == KIND_CELL_MAJOR) ? P.W * cell.off : 0;
   }
@@ -138,71 +153,75 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  // ---- this lane's query row ---------------------------------------------
-  const int qlocal = wave * 32 + l32;
-  const bool qvalid = qlocal < qn;
-  const bool wave_active = wave * 32 < qn;
-  int qtok = 0;
-  if (qvalid) qtok = ranged ? (q0 + qlocal) : cell_token(P, cell, q0 + qlocal);
-
-  bf16x8 qb[D / 16];
-  {
-    const uint16_t* qrow = Qb + (int64_t)qtok * P.q_st + 8 * hi;
+  // ---- this lane's query rows (one per query block) -----------------------
+  int qlocal[QB], qtok[QB];
+  bool qvalid[QB];
+  bf16x8 qb[QB][D / 16];
+#pragma unroll
+  for (int b = 0; b < QB; ++b) {
+    qlocal[b] = wave * 32 * QB + 32 * b + l32;
+    qvalid[b] = qlocal[b] < qn;
+    qtok[b] = 0;
+    if (qvalid[b]) qtok[b] = ranged ? (q0 + qlocal[b]) : cell_token(P, cell, q0 + qlocal[b]);
+    const uint16_t* qrow = Qb + (int64_t)qtok[b] * P.q_st + 8 * hi;
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
       u32x4 w = {0u, 0u, 0u, 0u};
-      if (qvalid) w = *(const u32x4*)(qrow + 16 * s);
-      qb[s] = __builtin_bit_cast(bf16x8, w);
+      if (qvalid[b]) w = *(const u32x4*)(qrow + 16 * s);
+      qb[b][s] = __builtin_bit_cast(bf16x8, w);
     }
   }
+  const bool wave_active = wave * 32 * QB < qn;
 
   // ---- staging assignments -------------------------------------------------
   const int kr0 = tid / TL::CPR, kch = tid % TL::CPR;      // K: rows kr0 + RPP*i, chunk kch
-  const int vo = tid / 16, va = tid % 16;                   // V: channels 8*vo.., keys 4*va..
   const bool vtask = tid < TL::VTASKS;
+  const int vo = (tid % TL::VTASKS) / 16, va = tid % 16;    // V: channels 8*vo.., keys 4*va..
 
-  // Contiguous key rows: a uniform (scalar) tile base plus a per-thread
-  // 32-bit byte offset; only the ragged last tile checks rows.
+  // Tile `it` covers keys [it*KTILE, min((it+1)*KTILE, kn)).  Its rows are
+  // loaded from lb(it) = min(it*KTILE, kn - KTILE): the ragged last tile is
+  // shifted back so every row it loads exists, and the keys it repeats are
+  // masked out of the softmax.  Loads are therefore unconditional, and the
+  // registers of the next tile's prefetch never pass through a branch (which
+  // would make the compiler wait for them before this tile's compute).  A key
+  // set shorter than one tile clamps its rows to the last key (and zeroes the
+  // copies once, before the loop), so no load ever leaves the key set.
+  const bool short_set = kn < KTILE;
+  const int rows_avail = short_set ? kn : KTILE;
+  auto tile_base = [&](int it) { return short_set ? 0 : min(it * KTILE, kn - KTILE); };
   const int64_t rowb = C.kv_st * 2;                       // bytes per key row
-  const uint32_t vko = (uint32_t)(kr0 * rowb + 16 * kch);
-  const uint32_t vvo = (uint32_t)(4 * va * rowb + 16 * vo);
+  uint32_t kofs[TL::KPASS], vofs[4];                      // per-thread byte offsets in a tile
+  int krow[TL::KPASS], vrow[4];                           // clamped row of each load in a tile
+#pragma unroll
+  for (int i = 0; i < TL::KPASS; ++i) {
+    krow[i] = min(kr0 + TL::RPP * i, rows_avail - 1);
+    kofs[i] = (uint32_t)(krow[i] * rowb + 16 * kch);
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    vrow[r] = min(4 * va + r, rows_avail - 1);
+    vofs[r] = (uint32_t)(vrow[r] * rowb + 16 * vo);
+  }
   const char* __restrict__ Kc = (const char*)Kb;
   const char* __restrict__ Vc = (const char*)Vb;
 
   u32x4 kreg[TL::KPASS];
   u32x4 vreg[4];
-  auto load_tile = [&](int kb) {
-    const u32x4 z = {0u, 0u, 0u, 0u};
+  auto load_tile = [&](int lb) {
     if constexpr (!GATHER) {
-      const char* kt = Kc + (int64_t)(k0 + kb) * rowb;
-      const char* vt = Vc + (int64_t)(k0 + kb) * rowb;
-      if (kb + KTILE <= kn) {
+      const char* kt = Kc + (int64_t)(k0 + lb) * rowb;   // uniform tile base
+      const char* vt = Vc + (int64_t)(k0 + lb) * rowb;
 #pragma unroll
-        for (int i = 0; i < TL::KPASS; ++i) kreg[i] = *(const u32x4*)(kt + i * TL::RPP * rowb + vko);
+      for (int i = 0; i < TL::KPASS; ++i) kreg[i] = *(const u32x4*)(kt + kofs[i]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          vreg[r] = (TL::VTASKS == NT || vtask) ? *(const u32x4*)(vt + r * rowb + vvo) : z;
-      } else {
-#pragma unroll
-        for (int i = 0; i < TL::KPASS; ++i)
-          kreg[i] = (kb + kr0 + TL::RPP * i < kn) ? *(const u32x4*)(kt + i * TL::RPP * rowb + vko) : z;
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          vreg[r] = (vtask && kb + 4 * va + r < kn) ? *(const u32x4*)(vt + r * rowb + vvo) : z;
-      }
+      for (int r = 0; r < 4; ++r) vreg[r] = *(const u32x4*)(vt + vofs[r]);
     } else {
 #pragma unroll
-      for (int i = 0; i < TL::KPASS; ++i) {
-        const int kk = kb + kr0 + TL::RPP * i;
-        kreg[i] = z;
-        if (kk < kn) kreg[i] = *(const u32x4*)(Kb + (int64_t)cell_token(P, cell, kk) * C.kv_st + 8 * kch);
-      }
+      for (int i = 0; i < TL::KPASS; ++i)
+        kreg[i] = *(const u32x4*)(Kb + (int64_t)cell_token(P, cell, lb + krow[i]) * C.kv_st + 8 * kch);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int kk = kb + 4 * va + r;
-        vreg[r] = z;
-        if (vtask && kk < kn) vreg[r] = *(const u32x4*)(Vb + (int64_t)cell_token(P, cell, kk) * C.kv_st + 8 * vo);
-      }
+      for (int r = 0; r < 4; ++r)
+        vreg[r] = *(const u32x4*)(Vb + (int64_t)cell_token(P, cell, lb + vrow[r]) * C.kv_st + 8 * vo);
     }
   };
   auto store_tile = [&](int buf) {
@@ -216,14 +235,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int w = e >> 1;
-        uint32_t x0 = vreg[0][w], x1 = vreg[1][w], x2 = vreg[2][w], x3 = vreg[3][w];
+        const uint32_t x0 = vreg[0][w], x1 = vreg[1][w], x2 = vreg[2][w], x3 = vreg[3][w];
         u32x2 pk;
-        if (e & 1) {
-          pk.x = (x0 >> 16) | (x1 & 0xffff0000u);
-          pk.y = (x2 >> 16) | (x3 & 0xffff0000u);
-        } else {
-          pk.x = (x0 & 0xffffu) | (x1 << 16);
-          pk.y = (x2 & 0xffffu) | (x3 << 16);
+        if (e & 1) {   // high halves of the four keys' words
+          pk.x = __builtin_amdgcn_perm(x1, x0, 0x07060302u);
+          pk.y = __builtin_amdgcn_perm(x3, x2, 0x07060302u);
+        } else {       // low halves
+          pk.x = __builtin_amdgcn_perm(x1, x0, 0x05040100u);
+          pk.y = __builtin_amdgcn_perm(x3, x2, 0x05040100u);
         }
         *(u32x2*)(Vt + (8 * vo + e) * TL::VS + pos) = pk;
       }
@@ -232,96 +251,125 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 
   // ---- main loop -------------------------------------------------------------
   const float c2 = P.scale_log2;
-  float m_run = -INFINITY;   // running max of raw scores for this lane's query
-  float l_run = 0.f;         // running sum over this lane's half of the keys
-  f32x16 oacc[D / 32];
+  float m_run[QB], l_run[QB];   // running max (raw scores) and this lane's half of the sum
+  f32x16 oacc[QB][D / 32];
 #pragma unroll
-  for (int t = 0; t < D / 32; ++t) oacc[t] = f32x16{};
+  for (int b = 0; b < QB; ++b) {
+    m_run[b] = -INFINITY;
+    l_run[b] = 0.f;
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t) oacc[b][t] = f32x16{};
+  }
 
   const int ntiles = (kn + KTILE - 1) / KTILE;
   load_tile(0);
+  if (short_set) {   // rows past the key set were clamped copies: zero them
+    const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < TL::KPASS; ++i)
+      if (kr0 + TL::RPP * i >= kn) kreg[i] = z;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (4 * va + r >= kn) vreg[r] = z;
+  }
   store_tile(0);
   __syncthreads();
 
   for (int it = 0; it < ntiles; ++it) {
     const int buf = it & 1;
-    const bool more = it + 1 < ntiles;
-    if (more) load_tile((it + 1) * KTILE);
+    // prefetch the next tile (the last iteration re-reads its own rows, unused)
+    load_tile(tile_base(min(it + 1, ntiles - 1)));
 
     if (wave_active) {
       const uint8_t* Ks = smem + buf * TL::BUF;
       const uint8_t* Vt = Ks + TL::KB;
-      f32x16 s0 = f32x16{}, s1 = f32x16{};
+      f32x16 sc[QB][2];
+#pragma unroll
+      for (int b = 0; b < QB; ++b) sc[b][0] = sc[b][1] = f32x16{};
 #pragma unroll
       for (int s = 0; s < D / 16; ++s) {
         const bf16x8 a0 = *(const bf16x8*)(Ks + l32 * TL::KS + (16 * s + 8 * hi) * 2);
         const bf16x8 a1 = *(const bf16x8*)(Ks + (32 + l32) * TL::KS + (16 * s + 8 * hi) * 2);
-        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qb[s], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qb[s], s1, 0, 0, 0);
+#pragma unroll
+        for (int b = 0; b < QB; ++b) {
+          sc[b][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qb[b][s], sc[b][0], 0, 0, 0);
+          sc[b][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qb[b][s], sc[b][1], 0, 0, 0);
+        }
       }
-      const int kb = it * KTILE;
-      if (kb + KTILE > kn) {   // ragged last tile: keys past the set get -inf
+      // Keys this tile must not count: rows repeated from the previous tile
+      // (shifted last tile, lb + j < it*KTILE) or past a short key set.
+      const int lo = it * KTILE - tile_base(it);   // slots j < lo are repeats
+      const int hi_end = short_set ? kn : KTILE;     // slots j >= hi_end are empty
+      if (lo > 0 || hi_end < KTILE) {
 #pragma unroll
         for (int jj = 0; jj < 16; ++jj) {
           const int key = 8 * (jj >> 2) + 4 * hi + (jj & 3);
-          if (kb + key >= kn) s0[jj] = -INFINITY;
-          if (kb + 32 + key >= kn) s1[jj] = -INFINITY;
+#pragma unroll
+          for (int b = 0; b < QB; ++b) {
+            if (key < lo || key >= hi_end) sc[b][0][jj] = -INFINITY;
+            if (key + 32 < lo || key + 32 >= hi_end) sc[b][1][jj] = -INFINITY;
+          }
         }
       }
-      float mx = s0[0];
+      bf16x8 pb[QB][4];
 #pragma unroll
-      for (int jj = 1; jj < 16; ++jj) mx = fmaxf(mx, s0[jj]);
+      for (int b = 0; b < QB; ++b) {
+        float mx = sc[b][0][0];
 #pragma unroll
-      for (int jj = 0; jj < 16; ++jj) mx = fmaxf(mx, s1[jj]);
-      {
-        const Pair pr = halves(mx);
-        mx = fmaxf(pr.a, pr.b);
-      }
-      const bool grow = mx * c2 > fmaf(m_run, c2, kLazyLog2);
-      if (__builtin_amdgcn_ballot_w64(grow) != 0) {   // wave-uniform
-        const float m_new = grow ? mx : m_run;
-        const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c2);
-        l_run *= alpha;
+        for (int jj = 1; jj < 16; ++jj) mx = fmaxf(mx, sc[b][0][jj]);
 #pragma unroll
-        for (int t = 0; t < D / 32; ++t) oacc[t] *= alpha;
-        m_run = m_new;
-      }
-      const float mc = m_run * c2;
-      float psum = 0.f;
+        for (int jj = 0; jj < 16; ++jj) mx = fmaxf(mx, sc[b][1][jj]);
+        {
+          const Pair pr = halves(mx);
+          mx = fmaxf(pr.a, pr.b);
+        }
+        const bool grow = mx * c2 > fmaf(m_run[b], c2, kLazyLog2);
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {   // wave-uniform
+          const float m_new = grow ? mx : m_run[b];
+          const float alpha = __builtin_amdgcn_exp2f((m_run[b] - m_new) * c2);
+          l_run[b] *= alpha;
 #pragma unroll
-      for (int jj = 0; jj < 16; ++jj) {
-        s0[jj] = __builtin_amdgcn_exp2f(fmaf(s0[jj], c2, -mc));
-        s1[jj] = __builtin_amdgcn_exp2f(fmaf(s1[jj], c2, -mc));
-        psum += s0[jj] + s1[jj];
-      }
-      l_run += psum;
-
-      bf16x8 pb[4];
+          for (int t = 0; t < D / 32; ++t) oacc[b][t] *= alpha;
+          m_run[b] = m_new;
+        }
+        const float mc = m_run[b] * c2;
+        float psum = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        pb[0][e] = (__bf16)s0[e];
-        pb[1][e] = (__bf16)s0[8 + e];
-        pb[2][e] = (__bf16)s1[e];
-        pb[3][e] = (__bf16)s1[8 + e];
+        for (int jj = 0; jj < 16; ++jj) {
+          sc[b][0][jj] = __builtin_amdgcn_exp2f(fmaf(sc[b][0][jj], c2, -mc));
+          sc[b][1][jj] = __builtin_amdgcn_exp2f(fmaf(sc[b][1][jj], c2, -mc));
+          psum += sc[b][0][jj] + sc[b][1][jj];
+        }
+        l_run[b] += psum;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          pb[b][0][e] = (__bf16)sc[b][0][e];
+          pb[b][1][e] = (__bf16)sc[b][0][8 + e];
+          pb[b][2][e] = (__bf16)sc[b][1][e];
+          pb[b][3][e] = (__bf16)sc[b][1][8 + e];
+        }
       }
 #pragma unroll
       for (int t = 0; t < D / 32; ++t) {
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
           const bf16x8 a = *(const bf16x8*)(Vt + (32 * t + l32) * TL::VS + (16 * kk + 8 * hi) * 2);
-          oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kk], oacc[t], 0, 0, 0);
+#pragma unroll
+          for (int b = 0; b < QB; ++b)
+            oacc[b][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[b][kk], oacc[b][t], 0, 0, 0);
         }
       }
     }
-    if (more) store_tile(buf ^ 1);
+    store_tile(buf ^ 1);
     __syncthreads();
   }
 
   // ---- epilogue -------------------------------------------------------------
-  float l_tot;
-  {
-    const Pair pr = halves(l_run);
-    l_tot = pr.a + pr.b;
+  float l_tot[QB];
+#pragma unroll
+  for (int b = 0; b < QB; ++b) {
+    const Pair pr = halves(l_run[b]);
+    l_tot[b] = pr.a + pr.b;
   }
   const int splits = ranged ? C.splits : 1;
 
@@ -329,19 +377,22 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     // Write this split's unnormalised partial; the last split to arrive merges.
     const int id = slot * P.q_tiles + tile;
     const int n_ids = C.n_heads * P.q_tiles;
-    float* po = C.part + ((int64_t)id * splits + split) * QTILE * D;
-    float* pml = C.part + (int64_t)n_ids * splits * QTILE * D + ((int64_t)id * splits + split) * QTILE * 2;
+    float* po = C.part + ((int64_t)id * splits + split) * QT * D;
+    float* pml = C.part + (int64_t)n_ids * splits * QT * D + ((int64_t)id * splits + split) * QT * 2;
     if (wave_active) {
 #pragma unroll
-      for (int t = 0; t < D / 32; ++t)
+      for (int b = 0; b < QB; ++b) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          f32x4 w4 = {oacc[t][4 * g], oacc[t][4 * g + 1], oacc[t][4 * g + 2], oacc[t][4 * g + 3]};
-          *(f32x4*)(po + qlocal * D + 32 * t + 8 * g + 4 * hi) = w4;
+        for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            f32x4 w4 = {oacc[b][t][4 * g], oacc[b][t][4 * g + 1], oacc[b][t][4 * g + 2], oacc[b][t][4 * g + 3]};
+            *(f32x4*)(po + qlocal[b] * D + 32 * t + 8 * g + 4 * hi) = w4;
+          }
+        if (hi == 0) {
+          pml[2 * qlocal[b]] = m_run[b];
+          pml[2 * qlocal[b] + 1] = l_tot[b];
         }
-      if (hi == 0) {
-        pml[2 * qlocal] = m_run;
-        pml[2 * qlocal + 1] = l_tot;
       }
     }
     __threadfence();
@@ -353,69 +404,58 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     __syncthreads();
     if (!s_last) return;
     __threadfence();
-    if (!qvalid) return;
-    // merge all splits for this lane's query (its half of the channels)
-    const float* pml0 = C.part + (int64_t)n_ids * splits * QTILE * D + (int64_t)id * splits * QTILE * 2;
-    float M = -INFINITY;
-    for (int s = 0; s < splits; ++s) M = fmaxf(M, pml0[s * QTILE * 2 + 2 * qlocal]);
-    float L = 0.f;
+    if (tid == 0) C.counters[id] = 0;   // ready for the next call
+    // merge all splits for this lane's queries (its half of the channels)
+    const float* pml0 = C.part + (int64_t)n_ids * splits * QT * D + (int64_t)id * splits * QT * 2;
 #pragma unroll
-    for (int t = 0; t < D / 32; ++t) oacc[t] = f32x16{};
-    for (int s = 0; s < splits; ++s) {
-      const float ms = pml0[s * QTILE * 2 + 2 * qlocal];
-      const float ls = pml0[s * QTILE * 2 + 2 * qlocal + 1];
-      const float w = __builtin_amdgcn_exp2f((ms - M) * c2);
-      L = fmaf(w, ls, L);
-      const float* ps = C.part + ((int64_t)id * splits + s) * QTILE * D + qlocal * D;
+    for (int b = 0; b < QB; ++b) {
+      if (!qvalid[b]) continue;
+      float M = -INFINITY;
+      for (int s = 0; s < splits; ++s) M = fmaxf(M, pml0[s * QT * 2 + 2 * qlocal[b]]);
+      float L = 0.f;
+      f32x4 acc[D / 32][4];
 #pragma unroll
       for (int t = 0; t < D / 32; ++t)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x4 x = *(const f32x4*)(ps + 32 * t + 8 * g + 4 * hi);
-          oacc[t][4 * g] = fmaf(w, x[0], oacc[t][4 * g]);
-          oacc[t][4 * g + 1] = fmaf(w, x[1], oacc[t][4 * g + 1]);
-          oacc[t][4 * g + 2] = fmaf(w, x[2], oacc[t][4 * g + 2]);
-          oacc[t][4 * g + 3] = fmaf(w, x[3], oacc[t][4 * g + 3]);
-        }
+        for (int g = 0; g < 4; ++g) acc[t][g] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int s = 0; s < splits; ++s) {
+        const float ms = pml0[s * QT * 2 + 2 * qlocal[b]];
+        const float ls = pml0[s * QT * 2 + 2 * qlocal[b] + 1];
+        const float w = __builtin_amdgcn_exp2f((ms - M) * c2);
+        L = fmaf(w, ls, L);
+        const float* ps = C.part + ((int64_t)id * splits + s) * QT * D + qlocal[b] * D;
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 x = *(const f32x4*)(ps + 32 * t + 8 * g + 4 * hi);
+            acc[t][g] += w * x;
+          }
+      }
+      const float inv = 1.f / L;
+      const int64_t obase = (int64_t)qh * C.o_sh + (int64_t)qtok[b] * C.o_st;
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) store_row4<OUT_F32>(C.o, obase + 32 * t + 8 * g + 4 * hi, acc[t][g] * inv);
     }
-    if (tid == 0) C.counters[id] = 0;   // ready for the next call
-    const float inv = 1.f / L;
-    uint8_t* orow = (uint8_t*)C.o;
-    const int64_t obase = (int64_t)qh * C.o_sh + (int64_t)qtok * C.o_st;
+    return;
+  }
+
+#pragma unroll
+  for (int b = 0; b < QB; ++b) {
+    if (!qvalid[b]) continue;
+    const float inv = 1.f / l_tot[b];
+    const int64_t obase = (int64_t)qh * C.o_sh + (int64_t)qtok[b] * C.o_st;
 #pragma unroll
     for (int t = 0; t < D / 32; ++t)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int ch = 32 * t + 8 * g + 4 * hi;
-        if (OUT_F32) {
-          f32x4 w4 = {oacc[t][4 * g] * inv, oacc[t][4 * g + 1] * inv, oacc[t][4 * g + 2] * inv, oacc[t][4 * g + 3] * inv};
-          *(f32x4*)((float*)orow + obase + ch) = w4;
-        } else {
-          bf16x4 b = {(__bf16)(oacc[t][4 * g] * inv), (__bf16)(oacc[t][4 * g + 1] * inv),
-                      (__bf16)(oacc[t][4 * g + 2] * inv), (__bf16)(oacc[t][4 * g + 3] * inv)};
-          *(u32x2*)((uint16_t*)orow + obase + ch) = __builtin_bit_cast(u32x2, b);
-        }
+        const f32x4 v = {oacc[b][t][4 * g] * inv, oacc[b][t][4 * g + 1] * inv, oacc[b][t][4 * g + 2] * inv,
+                         oacc[b][t][4 * g + 3] * inv};
+        store_row4<OUT_F32>(C.o, obase + 32 * t + 8 * g + 4 * hi, v);
       }
-    return;
   }
-
-  if (!qvalid) return;
-  const float inv = 1.f / l_tot;
-  const int64_t obase = (int64_t)qh * C.o_sh + (int64_t)qtok * C.o_st;
-#pragma unroll
-  for (int t = 0; t < D / 32; ++t)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int ch = 32 * t + 8 * g + 4 * hi;
-      if (OUT_F32) {
-        f32x4 w4 = {oacc[t][4 * g] * inv, oacc[t][4 * g + 1] * inv, oacc[t][4 * g + 2] * inv, oacc[t][4 * g + 3] * inv};
-        *(f32x4*)((float*)C.o + obase + ch) = w4;
-      } else {
-        bf16x4 b = {(__bf16)(oacc[t][4 * g] * inv), (__bf16)(oacc[t][4 * g + 1] * inv),
-                    (__bf16)(oacc[t][4 * g + 2] * inv), (__bf16)(oacc[t][4 * g + 3] * inv)};
-        *(u32x2*)((uint16_t*)C.o + obase + ch) = __builtin_bit_cast(u32x2, b);
-      }
-    }
 }
 
 }  // namespace
@@ -427,7 +467,7 @@ hipError_t launch_attn_bf16(const AttnPlan& plan, int head_dim, hipStream_t s) {
   for (int c = 1; c < plan.n_cats; ++c)
     if ((plan.cat[c].kind == KIND_CELL_GATHER) != gather) return hipErrorInvalidValue;  // one mode per launch
   dim3 grid(plan.total_units), block(NT);
-#define HC_LAUNCH(DD, F, G) hipLaunchKernelGGL((attn_bf16_kernel<DD, F, G>), grid, block, 0, s, plan)
+#define HC_LAUNCH(DD, F, G) hipLaunchKernelGGL((attn_bf16_kernel<DD, kBf16QueryBlocks, F, G>), grid, block, 0, s, plan)
   if (head_dim == 128) {
     if (gather) { if (f32) HC_LAUNCH(128, true, true); else HC_LAUNCH(128, false, true); }
     else { if (f32) HC_LAUNCH(128, true, false); else HC_LAUNCH(128, false, false); }

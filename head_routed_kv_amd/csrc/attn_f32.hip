@@ -59,8 +59,8 @@ __global__ __launch_bounds__(NT) void attn_f32_kernel(const AttnPlan P) {
   if (ranged) {
     const int split = j / P.q_tiles;
     const int tile = j - split * P.q_tiles;
-    q0 = tile * QTILE;
-    qn = min(QTILE, P.Nq - q0);
+    q0 = tile * QTILE_F32;
+    qn = min(QTILE_F32, P.Nq - q0);
     k0 = C.kv_first;
     kn = C.kv_count;   // this kernel never splits the key range
     (void)split;
@@ -68,10 +68,10 @@ __global__ __launch_bounds__(NT) void attn_f32_kernel(const AttnPlan P) {
     const int c = j / P.cell_subtiles;
     const int st = j - c * P.cell_subtiles;
     cell = cell_info(P, c);
-    q0 = st * QTILE;
+    q0 = st * QTILE_F32;
     const int qall = P.B * cell.size;
     if (q0 >= qall) return;
-    qn = min(QTILE, qall - q0);
+    qn = min(QTILE_F32, qall - q0);
     kn = C.kv_count * cell.size;
     k0 = (C.kind == KIND_CELL_MAJOR) ? P.W * cell.off : 0;
   }

@@ -25,8 +25,10 @@ namespace hc {
 // ---------------------------------------------------------------------------
 enum : int32_t { KIND_RANGED = 0, KIND_CELL_MAJOR = 1, KIND_CELL_GATHER = 2 };
 
-constexpr int QTILE = 128;  // queries per work group (4 waves x 32)
-constexpr int KTILE = 64;   // keys per inner iteration
+constexpr int kBf16QueryBlocks = 1;                  // 32-query blocks per wave, bf16 kernel
+constexpr int QTILE_BF16 = 128 * kBf16QueryBlocks;   // queries per work group, bf16 kernel
+constexpr int QTILE_F32 = 128;                       // queries per work group, fp32 kernel
+constexpr int KTILE = 64;                            // keys per inner iteration
 
 struct AttnCat {
   int32_t kind;
@@ -42,7 +44,7 @@ struct AttnCat {
   int64_t kv_sh, kv_st;   // slot (head) stride and token stride, elements
   void* o;                // output base for this category
   int64_t o_sh, o_st;     // output head / token strides, elements
-  float* part;            // split partials: [tile_id][splits][QTILE][D] fp32, then m,l
+  float* part;            // split partials: [tile_id][splits][q tile][D] fp32, then (m,l) pairs
   int32_t* counters;      // one per (head slot, q tile) when splits > 1
   int32_t out_f32;        // output written as fp32 (else the input dtype)
   int32_t pad_;
@@ -51,7 +53,7 @@ struct AttnCat {
 struct AttnPlan {
   int32_t n_cats;
   int32_t total_units;
-  int32_t q_tiles;         // ceil(Nq / QTILE), for ranged categories
+  int32_t q_tiles;         // ceil(Nq / queries per work group), for ranged categories
   int32_t cell_subtiles;   // q sub-tiles per spatial cell
   // Q
   const void* q;
