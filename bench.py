@@ -114,6 +114,25 @@ def make_flush(device):
     return flush
 
 
+def counter_traffic(workload):
+    """HBM bytes per launch of the attention kernel from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE record, scaled by its copy calibration.
+    None unless the record's source hash matches the sources built now (the
+    counters describe a kernel that no longer exists otherwise) and it was
+    taken on this workload."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"traffic_attn_bf16_{workload}_routed.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    h = hashlib.sha256()
+    for src in rec["sources"]:
+        h.update(open(os.path.join(ROOT, src), "rb").read())
+    if h.hexdigest() != rec["sources_sha256"]:
+        return None
+    return int(rec["traffic_bytes"])
+
+
 def cpu_baseline(wl, labels, seed, budget_s=20.0):
     """The oracle (fp64 numpy) on a bounded sample: every head, a seeded
     sample of query rows, timed on this host."""
@@ -268,8 +287,10 @@ def main():
                    "window_frames": wl.window_frames, "queries": wl.Nq, "keys": wl.Nk,
                    "labels": [int(x) for x in labels], "step": "append(REPLACE_NEWEST) + attend"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                     "kernel": "attn_bf16_kernel<128,false>", "attend_ms": round(attend_ms, 4),
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": counter_traffic(a.workload),
+                     "kernel": "attn_bf16_kernel", "attend_ms": round(attend_ms, 4),
+                     "traffic_unit": "bytes per launch (FETCH_SIZE x2.0 + WRITE_SIZE x1.0)",
+                     "algorithmic_bytes": sum(b for _, b in work.values()),
                      "algorithmic_flops": flops},
         "attend_cold_ms": round(cold_ms, 4),
         "full_attention": {"ms": round(full_ms, 4), "ms_cold": round(full_cold_ms, 4),
