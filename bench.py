@@ -264,6 +264,22 @@ def main():
                           "attend_ms": round(at2, 3), "tflops": round(f2 / (at2 / 1e3) / 1e12, 1),
                           "mfma_frac": round(f2 / (at2 / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
         del l2, q2, k2, v2
+        torch.cuda.empty_cache()
+        # one-shot classifier at the 720p shape, 40 heads (full + 3 proxy outputs, cosines, rule)
+        wl3 = W.WORKLOADS["classifier720p"]
+        q3, k3, v3 = gen_inputs(wl3, a.seed + 2, dev)
+        cfg3 = hk.make_config(wl3.heads, wl3.head_dim, wl3.grid_h, wl3.grid_w, wl3.block_frames, wl3.window_frames)
+        ws = None
+        for _ in range(2):
+            _, _, ws = hk.classify(cfg3, q3, k3, v3, workspace=ws)
+        cls_ms = time_events(lambda: hk.classify(cfg3, q3, k3, v3, workspace=ws), 3)
+        BT = wl3.Nq
+        pairs = wl3.Nq * wl3.Nk + 2 * wl3.Nq * BT + \
+            wl3.block_frames * wl3.window_frames * sum(c * c for c in cell_sizes(wl3.grid_h, wl3.grid_w))
+        f3 = wl3.heads * 4 * wl3.head_dim * pairs
+        extra["classifier720p"] = {"heads": wl3.heads, "ms": round(cls_ms, 3), "tflops": round(f3 / (cls_ms / 1e3) / 1e12, 1),
+                                   "mfma_frac": round(f3 / (cls_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        del q3, k3, v3, ws
 
     cpu = None
     if not a.no_cpu:

@@ -11,13 +11,22 @@
 // double-buffered LDS with online softmax.  Per wave and key tile:
 //   S^T (64 keys x 32 queries) = K_tile . Q^T      per query block: 2 x D/16 v_mfma_f32_32x32x16_bf16
 //   O^T (D x 32)             += V_tile^T . P^T     per query block: D/32 x 4 MFMAs
-// Every K and V^T operand read from LDS feeds all QB query blocks, so LDS
-// bytes per MFMA fall as 1/QB (the LDS read port, not the matrix core, bounds
-// a 32-query wave).  Computing S transposed puts one query per lane (32
-// scores per lane, the other 32 of the tile in lane^32), so the row max needs
-// one v_permlane32_swap and rescaling O is a per-lane scalar.  V is transposed
-// while being staged into LDS, with bits 2 and 3 of the key index swapped so
-// that every MFMA operand read is a single 16-byte LDS load.
+// Computing S transposed puts one query per lane (32 scores per lane, the
+// other 32 of the tile in lane^32), so the row max needs one
+// v_permlane32_swap and rescaling O is a per-lane scalar.
+//
+// K and V tiles go from global memory straight into LDS (global_load_lds,
+// 16 bytes per lane; lane l of a load lands at byte 16*l of its 1 KiB slot),
+// so staging costs no registers and no LDS write instructions, and the next
+// tile's loads run behind the current tile's math.  Rows keep their natural
+// [key][channel] layout; 16-byte chunks are XOR-swizzled per row (chunk c of
+// row r sits at slot c ^ sw(r)) so that both read patterns are free of bank
+// conflicts.  The K operand of S^T is one 16-byte read per lane.  The V^T
+// operand of O^T is two ds_read_b64_tr_b16 per lane: that instruction
+// transposes 4x4 blocks of 16-bit values across each group of 16 lanes (lane
+// i receives element i&3 of the 8-byte chunks addressed by lanes (i>>2)+4e,
+// e = 0..3), so lanes addressing 4 consecutive keys x 16 channels receive 4
+// keys of one channel each, which is the MFMA operand layout.
 #include "hc_internal.h"
 
 namespace hc {
@@ -35,20 +44,29 @@ constexpr int NT = 256;  // threads per work group
 template <int D>
 struct Tile {
   static constexpr int CPR = D / 8;            // 16-byte chunks per key row
-  static constexpr int RPP = NT / CPR;         // K rows loaded per pass
-  static constexpr int KPASS = KTILE / RPP;    // K load passes per thread
-  static constexpr int KS = D * 2 + 16;        // LDS bytes per K row (padded)
-  static constexpr int VS = KTILE * 2 + 16;    // LDS bytes per V^T row (padded)
-  static constexpr int KB = KTILE * KS;
-  static constexpr int VB = D * VS;
-  static constexpr int BUF = KB + VB;
-  static constexpr int VTASKS = (KTILE / 4) * CPR;  // (4 keys x 8 channels) tasks
+  static constexpr int ROWB = D * 2;           // LDS bytes per key row (unpadded)
+  static constexpr int RPI = 64 / CPR;         // rows per 1 KiB direct load (64 lanes x 16 B)
+  static constexpr int KB = KTILE * ROWB;      // K tile bytes
+  static constexpr int BUF = 2 * KB;           // K tile + V tile
+  static constexpr int LPW = KB / 1024 / 4;    // direct loads per wave per tile, for K (same for V)
+  static_assert(LPW >= 1, "tile too small");
 };
 
-// Position of key k (0..63) inside a V^T row: bits 2 and 3 swapped.
-__device__ __forceinline__ int vpos(int k) {
-  return (k & ~12) | ((k >> 1) & 4) | ((k << 1) & 8);
+typedef uint8_t __attribute__((address_space(3))) lds_u8;
+
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes land
+// at dst + 16*l (dst is wave-uniform).  A plain device function: inside a
+// kernel template the builtin keeps the host pass from emitting the launch stub.
+__device__ __forceinline__ void lds_dma16(const void* src, lds_u8* dst) {
+  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
 }
+
+// Chunk swizzles: K reads take 16 consecutive rows at one chunk, V reads take
+// 4 consecutive rows at two neighbouring chunks.
+template <int D>
+__device__ __forceinline__ int swz_k(int r) { return r & (Tile<D>::CPR - 1); }
+template <int D>
+__device__ __forceinline__ int swz_v(int r) { return (2 * r) & (Tile<D>::CPR - 1); }
 
 struct CellInfo {
   int base;    // y0*grid_w + x0
@@ -106,7 +124,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(QB == 1 ? 2 
 void attn_bf16_kernel(const AttnPlan P) {
   using TL = Tile<D>;
   constexpr int QT = 128 * QB;   // queries per work group
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * TL::BUF];
+  // Two distinct LDS objects (not one indexed array), so the compiler can see
+  // that the next tile's LDS-DMA writes never alias this tile's reads and does
+  // not make the reads wait for the loads.
+  __shared__ __attribute__((aligned(16))) uint8_t smem0[TL::BUF];
+  __shared__ __attribute__((aligned(16))) uint8_t smem1[TL::BUF];
   __shared__ int s_last;
 
   const int u = blockIdx.x;
@@ -173,80 +195,60 @@ void attn_bf16_kernel(const AttnPlan P) {
   }
   const bool wave_active = wave * 32 * QB < qn;
 
-  // ---- staging assignments -------------------------------------------------
-  const int kr0 = tid / TL::CPR, kch = tid % TL::CPR;      // K: rows kr0 + RPP*i, chunk kch
-  const bool vtask = tid < TL::VTASKS;
-  const int vo = (tid % TL::VTASKS) / 16, va = tid % 16;    // V: channels 8*vo.., keys 4*va..
-
+  // ---- staging ---------------------------------------------------------------
   // Tile `it` covers keys [it*KTILE, min((it+1)*KTILE, kn)).  Its rows are
   // loaded from lb(it) = min(it*KTILE, kn - KTILE): the ragged last tile is
   // shifted back so every row it loads exists, and the keys it repeats are
-  // masked out of the softmax.  Loads are therefore unconditional, and the
-  // registers of the next tile's prefetch never pass through a branch (which
-  // would make the compiler wait for them before this tile's compute).  A key
-  // set shorter than one tile clamps its rows to the last key (and zeroes the
-  // copies once, before the loop), so no load ever leaves the key set.
+  // masked out of the softmax.  A key set shorter than one tile loads row
+  // min(r, kn-1) into slot r; the copies are masked too, and their values are
+  // finite, so they add exactly zero.  No load ever leaves the key set.
   const bool short_set = kn < KTILE;
   const int rows_avail = short_set ? kn : KTILE;
   auto tile_base = [&](int it) { return short_set ? 0 : min(it * KTILE, kn - KTILE); };
-  const int64_t rowb = C.kv_st * 2;                       // bytes per key row
-  uint32_t kofs[TL::KPASS], vofs[4];                      // per-thread byte offsets in a tile
-  int krow[TL::KPASS], vrow[4];                           // clamped row of each load in a tile
+  const int64_t rowb = C.kv_st * 2;                 // bytes per key row in global memory
+  // Direct load i of this wave fills rows [RPI*(4*i+wave), +RPI) of a tile; this
+  // lane writes slot (lane % CPR) of row (RPI*(4*i+wave) + lane / CPR).
+  int lrow[TL::LPW];
+  uint32_t kofs[TL::LPW], vofs[TL::LPW];
 #pragma unroll
-  for (int i = 0; i < TL::KPASS; ++i) {
-    krow[i] = min(kr0 + TL::RPP * i, rows_avail - 1);
-    kofs[i] = (uint32_t)(krow[i] * rowb + 16 * kch);
-  }
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    vrow[r] = min(4 * va + r, rows_avail - 1);
-    vofs[r] = (uint32_t)(vrow[r] * rowb + 16 * vo);
+  for (int i = 0; i < TL::LPW; ++i) {
+    const int r = TL::RPI * (4 * i + wave) + lane / TL::CPR;
+    const int slot_c = lane % TL::CPR;
+    lrow[i] = min(r, rows_avail - 1);
+    kofs[i] = (uint32_t)(lrow[i] * rowb + 16 * (slot_c ^ swz_k<D>(r)));
+    vofs[i] = (uint32_t)(lrow[i] * rowb + 16 * (slot_c ^ swz_v<D>(r)));
   }
   const char* __restrict__ Kc = (const char*)Kb;
   const char* __restrict__ Vc = (const char*)Vb;
-
-  u32x4 kreg[TL::KPASS];
-  u32x4 vreg[4];
-  auto load_tile = [&](int lb) {
+  auto load_tile = [&](int lb, uint8_t* dst) {
+    lds_u8* kdst = (lds_u8*)dst;
+    lds_u8* vdst = kdst + TL::KB;
     if constexpr (!GATHER) {
       const char* kt = Kc + (int64_t)(k0 + lb) * rowb;   // uniform tile base
       const char* vt = Vc + (int64_t)(k0 + lb) * rowb;
 #pragma unroll
-      for (int i = 0; i < TL::KPASS; ++i) kreg[i] = *(const u32x4*)(kt + kofs[i]);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) vreg[r] = *(const u32x4*)(vt + vofs[r]);
+      for (int i = 0; i < TL::LPW; ++i) {
+        lds_dma16(kt + kofs[i], kdst + 1024 * (4 * i + wave));
+        lds_dma16(vt + vofs[i], vdst + 1024 * (4 * i + wave));
+      }
     } else {
 #pragma unroll
-      for (int i = 0; i < TL::KPASS; ++i)
-        kreg[i] = *(const u32x4*)(Kb + (int64_t)cell_token(P, cell, lb + krow[i]) * C.kv_st + 8 * kch);
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        vreg[r] = *(const u32x4*)(Vb + (int64_t)cell_token(P, cell, lb + vrow[r]) * C.kv_st + 8 * vo);
-    }
-  };
-  auto store_tile = [&](int buf) {
-    uint8_t* Ks = smem + buf * TL::BUF;
-    uint8_t* Vt = Ks + TL::KB;
-#pragma unroll
-    for (int i = 0; i < TL::KPASS; ++i)
-      *(u32x4*)(Ks + (kr0 + TL::RPP * i) * TL::KS + 16 * kch) = kreg[i];
-    if (vtask) {
-      const int pos = vpos(4 * va) * 2;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int w = e >> 1;
-        const uint32_t x0 = vreg[0][w], x1 = vreg[1][w], x2 = vreg[2][w], x3 = vreg[3][w];
-        u32x2 pk;
-        if (e & 1) {   // high halves of the four keys' words
-          pk.x = __builtin_amdgcn_perm(x1, x0, 0x07060302u);
-          pk.y = __builtin_amdgcn_perm(x3, x2, 0x07060302u);
-        } else {       // low halves
-          pk.x = __builtin_amdgcn_perm(x1, x0, 0x05040100u);
-          pk.y = __builtin_amdgcn_perm(x3, x2, 0x05040100u);
-        }
-        *(u32x2*)(Vt + (8 * vo + e) * TL::VS + pos) = pk;
+      for (int i = 0; i < TL::LPW; ++i) {
+        const int r = TL::RPI * (4 * i + wave) + lane / TL::CPR;
+        const int slot_c = lane % TL::CPR;
+        const int64_t row = (int64_t)cell_token(P, cell, lb + lrow[i]) * rowb;
+        lds_dma16(Kc + row + 16 * (slot_c ^ swz_k<D>(r)), kdst + 1024 * (4 * i + wave));
+        lds_dma16(Vc + row + 16 * (slot_c ^ swz_v<D>(r)), vdst + 1024 * (4 * i + wave));
       }
     }
+  };
+  // LDS address of the V^T operand half q (keys +0..3 or +8..11 of a 16-key
+  // step) for d-tile t and k-step kk, relative to the V tile.
+  const int vg = lane >> 4, vj = lane & 15;
+  auto vt_addr = [&](int t, int kk, int q) {
+    const int row = 16 * kk + 8 * q + 4 * (vg >> 1) + (vj >> 2);
+    const int col = 32 * t + 16 * (vg & 1) + 4 * (vj & 3);
+    return row * TL::ROWB + 16 * ((col >> 3) ^ swz_v<D>(row)) + 2 * (col & 7);
   };
 
   // ---- main loop -------------------------------------------------------------
@@ -262,34 +264,26 @@ void attn_bf16_kernel(const AttnPlan P) {
   }
 
   const int ntiles = (kn + KTILE - 1) / KTILE;
-  load_tile(0);
-  if (short_set) {   // rows past the key set were clamped copies: zero them
-    const u32x4 z = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int i = 0; i < TL::KPASS; ++i)
-      if (kr0 + TL::RPP * i >= kn) kreg[i] = z;
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      if (4 * va + r >= kn) vreg[r] = z;
-  }
-  store_tile(0);
+  load_tile(0, smem0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
-  for (int it = 0; it < ntiles; ++it) {
-    const int buf = it & 1;
-    // prefetch the next tile (the last iteration re-reads its own rows, unused)
-    load_tile(tile_base(min(it + 1, ntiles - 1)));
+  // One key tile: prefetch the next tile into `nxt` (the last tile re-reads its
+  // own rows, unused), then the math on `cur` runs behind those loads.
+  auto step = [&](const int it, const uint8_t* cur, uint8_t* nxt) {
+    load_tile(tile_base(min(it + 1, ntiles - 1)), nxt);
 
     if (wave_active) {
-      const uint8_t* Ks = smem + buf * TL::BUF;
-      const uint8_t* Vt = Ks + TL::KB;
+      const uint8_t* Ks = cur;
+      const uint8_t* Vt = cur + TL::KB;
       f32x16 sc[QB][2];
 #pragma unroll
       for (int b = 0; b < QB; ++b) sc[b][0] = sc[b][1] = f32x16{};
 #pragma unroll
       for (int s = 0; s < D / 16; ++s) {
-        const bf16x8 a0 = *(const bf16x8*)(Ks + l32 * TL::KS + (16 * s + 8 * hi) * 2);
-        const bf16x8 a1 = *(const bf16x8*)(Ks + (32 + l32) * TL::KS + (16 * s + 8 * hi) * 2);
+        const int c = 2 * s + hi;
+        const bf16x8 a0 = *(const bf16x8*)(Ks + l32 * TL::ROWB + 16 * (c ^ swz_k<D>(l32)));
+        const bf16x8 a1 = *(const bf16x8*)(Ks + (32 + l32) * TL::ROWB + 16 * (c ^ swz_k<D>(32 + l32)));
 #pragma unroll
         for (int b = 0; b < QB; ++b) {
           sc[b][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qb[b][s], sc[b][0], 0, 0, 0);
@@ -353,15 +347,25 @@ void attn_bf16_kernel(const AttnPlan P) {
       for (int t = 0; t < D / 32; ++t) {
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-          const bf16x8 a = *(const bf16x8*)(Vt + (32 * t + l32) * TL::VS + (16 * kk + 8 * hi) * 2);
+          typedef short s16x4 __attribute__((ext_vector_type(4)));
+          typedef short __attribute__((address_space(3))) lds_s16;
+          const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (s16x4 __attribute__((address_space(3)))*)((lds_u8*)Vt + vt_addr(t, kk, 0)));
+          const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (s16x4 __attribute__((address_space(3)))*)((lds_u8*)Vt + vt_addr(t, kk, 1)));
+          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
           for (int b = 0; b < QB; ++b)
             oacc[b][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[b][kk], oacc[b][t], 0, 0, 0);
         }
       }
     }
-    store_tile(buf ^ 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's share of the next tile is in LDS
     __syncthreads();
+  };
+  for (int it = 0; it < ntiles; it += 2) {
+    step(it, smem0, smem1);
+    if (it + 1 < ntiles) step(it + 1, smem1, smem0);
   }
 
   // ---- epilogue -------------------------------------------------------------
