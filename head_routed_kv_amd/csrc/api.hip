@@ -38,9 +38,9 @@ size_t elt_size(int dtype) { return dtype == HC_BF16 ? 2 : 4; }
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
-// The split plan is made for the 256 compute units of an MI355X, one work
-// group of the bf16 attention kernel per compute unit.
-constexpr int kWorkGroupSlots = 256 * (kBf16QueryBlocks == 1 ? 2 : 1);
+// The split plan is made for the 256 compute units of an MI355X and the
+// number of bf16 attention work groups resident per compute unit.
+constexpr int kWorkGroupSlots = 256 * kBf16GroupsPerCU;
 constexpr int kMaxSplits = 8;
 
 hc_status check_config(const hc_config* c) {

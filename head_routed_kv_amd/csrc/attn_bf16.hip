@@ -6,9 +6,10 @@
 // carries the argument" and Fig. 3: per-head pathways, non-overlapping grid
 // cells).
 //
-// A work group is 4 waves; each wave owns QB blocks of 32 queries, so a work
-// group owns 128*QB queries and streams the key set in 64-key tiles through
-// double-buffered LDS with online softmax.  Per wave and key tile:
+// A work group is NW waves; each wave owns QB blocks of 32 queries, so a work
+// group owns 32*QB*NW queries and streams the key set in 64-key tiles through
+// a ring of three LDS buffers (loads run two tiles ahead) with online
+// softmax.  Per wave and key tile:
 //   S^T (64 keys x 32 queries) = K_tile . Q^T      per query block: 2 x D/16 v_mfma_f32_32x32x16_bf16
 //   O^T (D x 32)             += V_tile^T . P^T     per query block: D/32 x 4 MFMAs
 // Computing S transposed puts one query per lane (32 scores per lane, the
@@ -39,7 +40,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int NT = 256;  // threads per work group
+constexpr int NW = kBf16Waves;   // waves per work group
+constexpr int NT = 64 * NW;      // threads per work group
+constexpr int NBUF = 3;          // LDS ring depth: loads run two tiles ahead
 
 template <int D>
 struct Tile {
@@ -48,17 +51,40 @@ struct Tile {
   static constexpr int RPI = 64 / CPR;         // rows per 1 KiB direct load (64 lanes x 16 B)
   static constexpr int KB = KTILE * ROWB;      // K tile bytes
   static constexpr int BUF = 2 * KB;           // K tile + V tile
-  static constexpr int LPW = KB / 1024 / 4;    // direct loads per wave per tile, for K (same for V)
+  static constexpr int LPW = KB / 1024 / NW;   // direct loads per wave per tile, for K (same for V)
   static_assert(LPW >= 1, "tile too small");
 };
 
 typedef uint8_t __attribute__((address_space(3))) lds_u8;
 
 // 16 bytes per lane from global memory straight into LDS: lane l's bytes land
-// at dst + 16*l (dst is wave-uniform).  A plain device function: inside a
-// kernel template the builtin keeps the host pass from emitting the launch stub.
-__device__ __forceinline__ void lds_dma16(const void* src, lds_u8* dst) {
-  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+// at LDS byte m0 + 16*l (m0 wave-uniform).  Written as one asm statement
+// with no output registers (the data goes to LDS), so the compiler's memory
+// counter bookkeeping does not see it: the kernel waits for these loads
+// itself (s_waitcnt vmcnt before each tile barrier) and otherwise the compiler
+// would wait for the newest tile's loads before every LDS read.  `base` is a
+// wave-uniform tile address, `voff` this lane's byte offset from it.
+__device__ __forceinline__ void lds_dma16(const char* base, uint32_t voff, uint32_t lds_byte) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(voff), "s"(base), "s"(lds_byte)
+      : "memory", "m0");
+}
+// The same for a per-lane 64-bit address (gathered rows).
+__device__ __forceinline__ void lds_dma16_addr(const char* addr, uint32_t lds_byte) {
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, off"
+      :
+      : "v"(addr), "s"(lds_byte)
+      : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
 // Chunk swizzles: K reads take 16 consecutive rows at one chunk, V reads take
@@ -120,15 +146,16 @@ __device__ __forceinline__ void store_row4(void* base, int64_t off, f32x4 v) {
 }
 
 template <int D, int QB, bool OUT_F32, bool GATHER>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(QB == 1 ? 2 : 1, QB == 1 ? 2 : 1)))
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2 / QB, 2 / QB)))
 void attn_bf16_kernel(const AttnPlan P) {
   using TL = Tile<D>;
-  constexpr int QT = 128 * QB;   // queries per work group
+  constexpr int QT = 32 * QB * NW;   // queries per work group
   // Two distinct LDS objects (not one indexed array), so the compiler can see
   // that the next tile's LDS-DMA writes never alias this tile's reads and does
   // not make the reads wait for the loads.
   __shared__ __attribute__((aligned(16))) uint8_t smem0[TL::BUF];
   __shared__ __attribute__((aligned(16))) uint8_t smem1[TL::BUF];
+  __shared__ __attribute__((aligned(16))) uint8_t smem2[TL::BUF];
   __shared__ int s_last;
 
   const int u = blockIdx.x;
@@ -171,7 +198,7 @@ void attn_bf16_kernel(const AttnPlan P) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
@@ -194,6 +221,10 @@ void attn_bf16_kernel(const AttnPlan P) {
     }
   }
   const bool wave_active = wave * 32 * QB < qn;
+  // Q has landed (vmcnt(0); expcnt and lgkmcnt untouched).  Said once here, in
+  // the form the compiler's wait bookkeeping understands, so the tile loop
+  // never waits for Q again.
+  __builtin_amdgcn_s_waitcnt(0x0F70);
 
   // ---- staging ---------------------------------------------------------------
   // Tile `it` covers keys [it*KTILE, min((it+1)*KTILE, kn)).  Its rows are
@@ -206,13 +237,13 @@ void attn_bf16_kernel(const AttnPlan P) {
   const int rows_avail = short_set ? kn : KTILE;
   auto tile_base = [&](int it) { return short_set ? 0 : min(it * KTILE, kn - KTILE); };
   const int64_t rowb = C.kv_st * 2;                 // bytes per key row in global memory
-  // Direct load i of this wave fills rows [RPI*(4*i+wave), +RPI) of a tile; this
+  // Direct load i of this wave fills rows [RPI*(NW*i+wave), +RPI) of a tile; this
   // lane writes slot (lane % CPR) of row (RPI*(4*i+wave) + lane / CPR).
   int lrow[TL::LPW];
   uint32_t kofs[TL::LPW], vofs[TL::LPW];
 #pragma unroll
   for (int i = 0; i < TL::LPW; ++i) {
-    const int r = TL::RPI * (4 * i + wave) + lane / TL::CPR;
+    const int r = TL::RPI * (NW * i + wave) + lane / TL::CPR;
     const int slot_c = lane % TL::CPR;
     lrow[i] = min(r, rows_avail - 1);
     kofs[i] = (uint32_t)(lrow[i] * rowb + 16 * (slot_c ^ swz_k<D>(r)));
@@ -221,24 +252,23 @@ void attn_bf16_kernel(const AttnPlan P) {
   const char* __restrict__ Kc = (const char*)Kb;
   const char* __restrict__ Vc = (const char*)Vb;
   auto load_tile = [&](int lb, uint8_t* dst) {
-    lds_u8* kdst = (lds_u8*)dst;
-    lds_u8* vdst = kdst + TL::KB;
+    const uint32_t kdst = lds_addr(dst), vdst = kdst + TL::KB;
     if constexpr (!GATHER) {
       const char* kt = Kc + (int64_t)(k0 + lb) * rowb;   // uniform tile base
       const char* vt = Vc + (int64_t)(k0 + lb) * rowb;
 #pragma unroll
       for (int i = 0; i < TL::LPW; ++i) {
-        lds_dma16(kt + kofs[i], kdst + 1024 * (4 * i + wave));
-        lds_dma16(vt + vofs[i], vdst + 1024 * (4 * i + wave));
+        lds_dma16(kt, kofs[i], kdst + 1024 * (NW * i + wave));
+        lds_dma16(vt, vofs[i], vdst + 1024 * (NW * i + wave));
       }
     } else {
 #pragma unroll
       for (int i = 0; i < TL::LPW; ++i) {
-        const int r = TL::RPI * (4 * i + wave) + lane / TL::CPR;
+        const int r = TL::RPI * (NW * i + wave) + lane / TL::CPR;
         const int slot_c = lane % TL::CPR;
         const int64_t row = (int64_t)cell_token(P, cell, lb + lrow[i]) * rowb;
-        lds_dma16(Kc + row + 16 * (slot_c ^ swz_k<D>(r)), kdst + 1024 * (4 * i + wave));
-        lds_dma16(Vc + row + 16 * (slot_c ^ swz_v<D>(r)), vdst + 1024 * (4 * i + wave));
+        lds_dma16_addr(Kc + row + 16 * (slot_c ^ swz_k<D>(r)), kdst + 1024 * (NW * i + wave));
+        lds_dma16_addr(Vc + row + 16 * (slot_c ^ swz_v<D>(r)), vdst + 1024 * (NW * i + wave));
       }
     }
   };
@@ -264,14 +294,30 @@ void attn_bf16_kernel(const AttnPlan P) {
   }
 
   const int ntiles = (kn + KTILE - 1) / KTILE;
+  // Each wave issues 2*LPW loads per tile; waiting until at most that many are
+  // in flight means every load but the newest tile's has landed in LDS.
+  auto wait_all_but_newest = [&]() {
+    if constexpr (2 * TL::LPW == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else if constexpr (2 * TL::LPW == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  };
+  // Tile barrier.  The LDS buffers are only written by the loads above, and
+  // every LDS read of a tile feeds that tile's MFMAs before the barrier, so a
+  // bare s_barrier orders the ring; __syncthreads() would also wait for the
+  // newest tile's loads and undo the two-tile lead.
+  auto tile_barrier = [&]() {
+    wait_all_but_newest();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
   load_tile(0, smem0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
+  load_tile(tile_base(min(1, ntiles - 1)), smem1);
+  tile_barrier();
 
-  // One key tile: prefetch the next tile into `nxt` (the last tile re-reads its
-  // own rows, unused), then the math on `cur` runs behind those loads.
-  auto step = [&](const int it, const uint8_t* cur, uint8_t* nxt) {
-    load_tile(tile_base(min(it + 1, ntiles - 1)), nxt);
+  // One key tile: prefetch tile it+2 into `nxt2` (past the end the last tile is
+  // re-read, unused), run the math on `cur`, then make tile it+1 visible.
+  auto step = [&](const int it, const uint8_t* cur, uint8_t* nxt2) {
+    load_tile(tile_base(min(it + 2, ntiles - 1)), nxt2);
 
     if (wave_active) {
       const uint8_t* Ks = cur;
@@ -360,13 +406,14 @@ void attn_bf16_kernel(const AttnPlan P) {
         }
       }
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's share of the next tile is in LDS
-    __syncthreads();
+    tile_barrier();   // tile it+1 is in LDS (all waves)
   };
-  for (int it = 0; it < ntiles; it += 2) {
-    step(it, smem0, smem1);
+  for (int it = 0; it < ntiles; it += 3) {
+    step(it, smem0, smem2);
     if (it + 1 < ntiles) step(it + 1, smem1, smem0);
+    if (it + 2 < ntiles) step(it + 2, smem2, smem1);
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no LDS load may outlive the work group
 
   // ---- epilogue -------------------------------------------------------------
   float l_tot[QB];
