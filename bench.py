@@ -124,13 +124,16 @@ def counter_traffic(workload):
     path = os.path.join(ROOT, "profiles", f"traffic_attn_bf16_{workload}_routed.json")
     if not os.path.exists(path):
         return None
-    rec = json.load(open(path))
-    h = hashlib.sha256()
-    for src in rec["sources"]:
-        h.update(open(os.path.join(ROOT, src), "rb").read())
-    if h.hexdigest() != rec["sources_sha256"]:
+    try:
+        rec = json.load(open(path))
+        h = hashlib.sha256()
+        for src in rec["sources"]:
+            h.update(open(os.path.join(ROOT, src), "rb").read())
+        if h.hexdigest() != rec["sources_sha256"]:
+            return None
+        return int(rec["traffic_bytes"])
+    except (OSError, ValueError, KeyError, TypeError):
         return None
-    return int(rec["traffic_bytes"])
 
 
 def cpu_baseline(wl, labels, seed, budget_s=20.0):

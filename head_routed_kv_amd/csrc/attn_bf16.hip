@@ -87,12 +87,15 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-// Chunk swizzles: K reads take 16 consecutive rows at one chunk, V reads take
-// 4 consecutive rows at two neighbouring chunks.
+// Chunk swizzles.  K reads: 16 lanes read one chunk of 16 consecutive rows, so
+// row r's chunks are XORed with r mod CPR.  V reads (transposing): 32 lanes
+// read the 4 aligned chunks {c0..c0+3} of 4 consecutive rows, so the 4 rows
+// must map that group onto disjoint slot groups: XOR with 4*(r&3) at 16 chunks
+// per row; at 8 chunks per row (two rows per bank sweep) with 4*((r>>1)&1).
 template <int D>
 __device__ __forceinline__ int swz_k(int r) { return r & (Tile<D>::CPR - 1); }
 template <int D>
-__device__ __forceinline__ int swz_v(int r) { return (2 * r) & (Tile<D>::CPR - 1); }
+__device__ __forceinline__ int swz_v(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 
 struct CellInfo {
   int base;    // y0*grid_w + x0
