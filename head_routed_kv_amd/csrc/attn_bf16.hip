@@ -8,8 +8,8 @@
 //
 // A work group is NW waves; each wave owns QB blocks of 32 queries, so a work
 // group owns 32*QB*NW queries and streams the key set in 64-key tiles through
-// a ring of three LDS buffers (loads run two tiles ahead) with online
-// softmax.  Per wave and key tile:
+// a ring of four LDS buffers with online softmax, software-pipelined so that
+// the scores of the next tile are computed alongside this tile's softmax.  Per wave and key tile:
 //   S^T (64 keys x 32 queries) = K_tile . Q^T      per query block: 2 x D/16 v_mfma_f32_32x32x16_bf16
 //   O^T (D x 32)             += V_tile^T . P^T     per query block: D/32 x 4 MFMAs
 // Computing S transposed puts one query per lane (32 scores per lane, the
@@ -42,7 +42,6 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int NW = kBf16Waves;   // waves per work group
 constexpr int NT = 64 * NW;      // threads per work group
-constexpr int NBUF = 3;          // LDS ring depth: loads run two tiles ahead
 
 template <int D>
 struct Tile {
@@ -159,6 +158,7 @@ void attn_bf16_kernel(const AttnPlan P) {
   __shared__ __attribute__((aligned(16))) uint8_t smem0[TL::BUF];
   __shared__ __attribute__((aligned(16))) uint8_t smem1[TL::BUF];
   __shared__ __attribute__((aligned(16))) uint8_t smem2[TL::BUF];
+  __shared__ __attribute__((aligned(16))) uint8_t smem3[TL::BUF];
   __shared__ int s_last;
 
   const int u = blockIdx.x;
@@ -305,41 +305,51 @@ void attn_bf16_kernel(const AttnPlan P) {
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   };
   // Tile barrier.  The LDS buffers are only written by the loads above, and
-  // every LDS read of a tile feeds that tile's MFMAs before the barrier, so a
-  // bare s_barrier orders the ring; __syncthreads() would also wait for the
-  // newest tile's loads and undo the two-tile lead.
+  // every LDS read of a tile feeds MFMAs issued before the barrier, so a bare
+  // s_barrier orders the ring; __syncthreads() would also wait for the newest
+  // tile's loads and undo their lead.
   auto tile_barrier = [&]() {
     wait_all_but_newest();
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
+  // S^T of one tile: sc[b][blk] (keys 32*blk.. x 32 queries of block b).
+  auto scores = [&](const uint8_t* Ks, f32x16 (&out)[QB][2]) {
+#pragma unroll
+    for (int b = 0; b < QB; ++b) out[b][0] = out[b][1] = f32x16{};
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      const int c = 2 * s + hi;
+      const bf16x8 a0 = *(const bf16x8*)(Ks + l32 * TL::ROWB + 16 * (c ^ swz_k<D>(l32)));
+      const bf16x8 a1 = *(const bf16x8*)(Ks + (32 + l32) * TL::ROWB + 16 * (c ^ swz_k<D>(32 + l32)));
+#pragma unroll
+      for (int b = 0; b < QB; ++b) {
+        out[b][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qb[b][s], out[b][0], 0, 0, 0);
+        out[b][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qb[b][s], out[b][1], 0, 0, 0);
+      }
+    }
+  };
+
+  // Software pipeline over key tiles, 4 LDS buffers (tile j lives in buffer
+  // j mod 4).  Step `it` holds V of tile it and K of tile it+1 while tile it+2
+  // is landing and tile it+3 is being loaded; it computes S of tile it+1 in
+  // the same instruction stream as the softmax of tile it, so the matrix core
+  // works while the vector unit exponentiates.  Tiles past the end are
+  // clamped copies of the last one (finite, unused).
   load_tile(0, smem0);
   load_tile(tile_base(min(1, ntiles - 1)), smem1);
-  tile_barrier();
+  load_tile(tile_base(min(2, ntiles - 1)), smem2);
+  tile_barrier();   // tiles 0 and 1 are in LDS
+  f32x16 sc[QB][2];
+  scores(smem0, sc);
 
-  // One key tile: prefetch tile it+2 into `nxt2` (past the end the last tile is
-  // re-read, unused), run the math on `cur`, then make tile it+1 visible.
-  auto step = [&](const int it, const uint8_t* cur, uint8_t* nxt2) {
-    load_tile(tile_base(min(it + 2, ntiles - 1)), nxt2);
+  const bf16x8 ones8 = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f,
+                        (__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
+  auto step = [&](const int it, const uint8_t* vbuf, const uint8_t* kbuf, uint8_t* lbuf) {
+    load_tile(tile_base(min(it + 3, ntiles - 1)), lbuf);
 
     if (wave_active) {
-      const uint8_t* Ks = cur;
-      const uint8_t* Vt = cur + TL::KB;
-      f32x16 sc[QB][2];
-#pragma unroll
-      for (int b = 0; b < QB; ++b) sc[b][0] = sc[b][1] = f32x16{};
-#pragma unroll
-      for (int s = 0; s < D / 16; ++s) {
-        const int c = 2 * s + hi;
-        const bf16x8 a0 = *(const bf16x8*)(Ks + l32 * TL::ROWB + 16 * (c ^ swz_k<D>(l32)));
-        const bf16x8 a1 = *(const bf16x8*)(Ks + (32 + l32) * TL::ROWB + 16 * (c ^ swz_k<D>(32 + l32)));
-#pragma unroll
-        for (int b = 0; b < QB; ++b) {
-          sc[b][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qb[b][s], sc[b][0], 0, 0, 0);
-          sc[b][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qb[b][s], sc[b][1], 0, 0, 0);
-        }
-      }
-      // Keys this tile must not count: rows repeated from the previous tile
+      // Keys tile `it` must not count: rows repeated from the previous tile
       // (shifted last tile, lb + j < it*KTILE) or past a short key set.
       const int lo = it * KTILE - tile_base(it);   // slots j < lo are repeats
       const int hi_end = short_set ? kn : KTILE;     // slots j >= hi_end are empty
@@ -354,7 +364,7 @@ void attn_bf16_kernel(const AttnPlan P) {
           }
         }
       }
-      bf16x8 pb[QB][4];
+      float mc[QB];
 #pragma unroll
       for (int b = 0; b < QB; ++b) {
         float mx = sc[b][0][0];
@@ -375,15 +385,20 @@ void attn_bf16_kernel(const AttnPlan P) {
           for (int t = 0; t < D / 32; ++t) oacc[b][t] *= alpha;
           m_run[b] = m_new;
         }
-        const float mc = m_run[b] * c2;
-        float psum = 0.f;
+        mc[b] = m_run[b] * c2;
+      }
+      // S of the next tile (matrix core) and P of this tile (vector unit):
+      // independent, one basic block, interleaved by the scheduler.
+      f32x16 sn[QB][2];
+      scores(kbuf, sn);
+      bf16x8 pb[QB][4];
+#pragma unroll
+      for (int b = 0; b < QB; ++b) {
 #pragma unroll
         for (int jj = 0; jj < 16; ++jj) {
-          sc[b][0][jj] = __builtin_amdgcn_exp2f(fmaf(sc[b][0][jj], c2, -mc));
-          sc[b][1][jj] = __builtin_amdgcn_exp2f(fmaf(sc[b][1][jj], c2, -mc));
-          psum += sc[b][0][jj] + sc[b][1][jj];
+          sc[b][0][jj] = __builtin_amdgcn_exp2f(fmaf(sc[b][0][jj], c2, -mc[b]));
+          sc[b][1][jj] = __builtin_amdgcn_exp2f(fmaf(sc[b][1][jj], c2, -mc[b]));
         }
-        l_run[b] += psum;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           pb[b][0][e] = (__bf16)sc[b][0][e];
@@ -391,30 +406,46 @@ void attn_bf16_kernel(const AttnPlan P) {
           pb[b][2][e] = (__bf16)sc[b][1][e];
           pb[b][3][e] = (__bf16)sc[b][1][8 + e];
         }
+        // row sum of the bf16 weights the PV product uses (2 per dot2)
+        float psum = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+            const bf16x2 p2 = {pb[b][kk][2 * e], pb[b][kk][2 * e + 1]};
+            const bf16x2 o2 = {ones8[0], ones8[1]};
+            psum = __builtin_amdgcn_fdot2_f32_bf16(p2, o2, psum, false);
+          }
+        l_run[b] += psum;
       }
+      // O^T += V^T P^T: k-steps outer, d-tiles inner, so consecutive MFMAs
+      // feed different accumulators.
 #pragma unroll
-      for (int t = 0; t < D / 32; ++t) {
+      for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
+        for (int t = 0; t < D / 32; ++t) {
           typedef short s16x4 __attribute__((ext_vector_type(4)));
-          typedef short __attribute__((address_space(3))) lds_s16;
           const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (s16x4 __attribute__((address_space(3)))*)((lds_u8*)Vt + vt_addr(t, kk, 0)));
+              (s16x4 __attribute__((address_space(3)))*)((lds_u8*)vbuf + TL::KB + vt_addr(t, kk, 0)));
           const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (s16x4 __attribute__((address_space(3)))*)((lds_u8*)Vt + vt_addr(t, kk, 1)));
+              (s16x4 __attribute__((address_space(3)))*)((lds_u8*)vbuf + TL::KB + vt_addr(t, kk, 1)));
           const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
           for (int b = 0; b < QB; ++b)
             oacc[b][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[b][kk], oacc[b][t], 0, 0, 0);
         }
       }
+#pragma unroll
+      for (int b = 0; b < QB; ++b) sc[b][0] = sn[b][0], sc[b][1] = sn[b][1];
     }
-    tile_barrier();   // tile it+1 is in LDS (all waves)
+    tile_barrier();   // tile it+2 is in LDS (all waves)
   };
-  for (int it = 0; it < ntiles; it += 3) {
-    step(it, smem0, smem2);
-    if (it + 1 < ntiles) step(it + 1, smem1, smem0);
-    if (it + 2 < ntiles) step(it + 2, smem2, smem1);
+  for (int it = 0; it < ntiles; it += 4) {
+    step(it, smem0, smem1, smem3);
+    if (it + 1 < ntiles) step(it + 1, smem1, smem2, smem0);
+    if (it + 2 < ntiles) step(it + 2, smem2, smem3, smem1);
+    if (it + 3 < ntiles) step(it + 3, smem3, smem0, smem2);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no LDS load may outlive the work group
 
