@@ -41,7 +41,8 @@ class hc_cache_layout(C.Structure):
                                           "off_dummy_k", "off_dummy_v", "off_spatial_k", "off_spatial_v",
                                           "off_scratch", "scratch_bytes")] + \
                [(n, C.c_int32) for n in ("n_global", "n_sink", "n_dummy", "n_spatial", "blocks_appended",
-                                         "global_splits")] + [("head_slot", C.c_int32 * HC_MAX_HEADS)]
+                                         "global_splits", "sink_splits", "dummy_splits")] + \
+               [("head_slot", C.c_int32 * HC_MAX_HEADS)]
 
 
 EXPORTS = {

@@ -41,7 +41,6 @@ int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 // The split plan is made for the 256 compute units of an MI355X and the
 // number of bf16 attention work groups resident per compute unit.
 constexpr int kWorkGroupSlots = 256 * kBf16GroupsPerCU;
-constexpr int kMaxSplits = 8;
 
 hc_status check_config(const hc_config* c) {
   if (!c) return fail(HC_ERR_INVALID_ARG, "config is NULL");
@@ -108,11 +107,11 @@ Geom geometry(const hc_config* c) {
 }
 
 // List-schedule the units of a full-window layer onto the work-group slots
-// (heaviest category first, as the kernel numbers them) and return the
-// makespan in key tiles.  Used to pick how many key-range splits the Global
-// heads get: enough units to keep every slot busy, not so many that the
-// partial-merge traffic dominates.
-double simulate(const hc_config* c, const Geom& g, const int count[4], int splits) {
+// in the order the bf16 kernel numbers them and return the makespan in key
+// tiles.  Used to pick how many key-range splits the ranged heads get: enough
+// units to keep every slot busy, not so many that writing and merging the
+// fp32 partials dominates (modelled as one key tile per split).
+double simulate(const hc_config* c, const Geom& g, const int count[4], const int splits[4]) {
   std::priority_queue<double, std::vector<double>, std::greater<double>> slots;
   for (int i = 0; i < kWorkGroupSlots; ++i) slots.push(0.0);
   auto run = [&](double cost, int64_t n) {
@@ -122,17 +121,19 @@ double simulate(const hc_config* c, const Geom& g, const int count[4], int split
       slots.push(t + cost);
     }
   };
-  const int key_tiles = cdiv(g.Nk, KTILE);
-  const int kps_tiles = cdiv(key_tiles, splits);
   const double fixed = 2.0;  // per-unit set-up and write-back, in key tiles
-  run(kps_tiles + fixed + (splits > 1 ? 0.5 * splits : 0.0), (int64_t)count[HC_GLOBAL] * g.q_tiles * splits);
-  run(cdiv(g.Nq, KTILE) + fixed, (int64_t)(count[HC_SINK] + count[HC_DUMMY]) * g.q_tiles);
-  for (int h = 0; h < count[HC_SPATIAL]; ++h)
-    for (int cl = 0; cl < g.n_cells; ++cl) {
-      const int qall = c->block_frames * g.cell_size[cl];
-      const int sub = cdiv(qall, qtile_of(c));
-      run(cdiv((int64_t)c->window_frames * g.cell_size[cl], KTILE) + fixed, sub);
-    }
+  auto ranged = [&](int lab, int key_tiles) {
+    const int s = splits[lab];
+    run(cdiv(key_tiles, s) + fixed + (s > 1 ? 1.0 * s : 0.0), (int64_t)count[lab] * g.q_tiles * s);
+  };
+  ranged(HC_GLOBAL, cdiv(g.Nk, KTILE));
+  ranged(HC_SINK, cdiv(g.Nq, KTILE));
+  ranged(HC_DUMMY, cdiv(g.Nq, KTILE));
+  for (int st = 0; st < g.cell_subtiles; ++st)   // the bf16 kernel's Spatial order
+    for (int h = 0; h < count[HC_SPATIAL]; ++h)
+      for (int cl = 0; cl < g.n_cells; ++cl)
+        if (st * qtile_of(c) < c->block_frames * g.cell_size[cl])
+          run(cdiv((int64_t)c->window_frames * g.cell_size[cl], KTILE) + fixed, 1);
   double mk = 0;
   while (!slots.empty()) {
     mk = std::max(mk, slots.top());
@@ -141,19 +142,29 @@ double simulate(const hc_config* c, const Geom& g, const int count[4], int split
   return mk;
 }
 
-int choose_splits(const hc_config* c, const Geom& g, const int count[4]) {
-  if (c->dtype != HC_BF16 || count[HC_GLOBAL] == 0) return 1;
-  int best = 1;
-  double best_t = simulate(c, g, count, 1);
-  for (int s = 2; s <= kMaxSplits; ++s) {
-    if (cdiv(g.Nk, KTILE) < 4 * s) break;  // each split keeps at least 4 key tiles
-    const double t = simulate(c, g, count, s);
-    if (t < 0.97 * best_t) {
-      best = s;
-      best_t = t;
+// Splits for Global heads first, then one count shared by Sink and Dummy
+// heads (same key-set size); a larger count is taken only if it shortens the
+// simulated makespan by 3% or more.  Each split keeps at least 4 key tiles.
+void choose_splits(const hc_config* c, const Geom& g, const int count[4], int splits[4]) {
+  for (int i = 0; i < 4; ++i) splits[i] = 1;
+  if (c->dtype != HC_BF16) return;
+  double best_t = simulate(c, g, count, splits);
+  auto search = [&](int lab_a, int lab_b, int key_tiles) {
+    if (count[lab_a] + count[lab_b] == 0) return;
+    int best = 1;
+    for (int s = 2; s <= kMaxSplits && key_tiles >= 4 * s; ++s) {
+      int trial[4] = {splits[0], splits[1], splits[2], splits[3]};
+      trial[lab_a] = trial[lab_b] = s;
+      const double t = simulate(c, g, count, trial);
+      if (t < 0.97 * best_t) {
+        best = s;
+        best_t = t;
+      }
     }
-  }
-  return best;
+    splits[lab_a] = splits[lab_b] = best;
+  };
+  search(HC_GLOBAL, HC_GLOBAL, cdiv(g.Nk, KTILE));
+  search(HC_SINK, HC_DUMMY, cdiv(g.Nq, KTILE));
 }
 
 struct Layout {
@@ -162,7 +173,9 @@ struct Layout {
   uint8_t head_of[4][HC_MAX_HEADS];
   size_t off_k[4], off_v[4], slot_bytes[4];
   size_t off_part = 0, off_counters = 0, scratch_bytes = 0, total = 0;
-  int splits = 1;
+  int splits[4] = {1, 1, 1, 1};         // key-range splits per archetype (Spatial: 1)
+  size_t part_at[4] = {0, 0, 0, 0};     // byte offset of each archetype's partials
+  int64_t counter_at[4] = {0, 0, 0, 0}; // first counter of each archetype
   int64_t n_counters = 0;
 };
 
@@ -187,17 +200,23 @@ hc_status make_layout(const hc_config* c, const int8_t* labels, Layout* L) {
     L->off_v[lab] = off;
     off = align256(off + L->count[lab] * L->slot_bytes[lab]);
   }
-  L->splits = choose_splits(c, g, L->count);
+  choose_splits(c, g, L->count, L->splits);
+  // Scratch: fp32 partials of each split archetype, then one int32 counter
+  // per (head, q tile) of every split archetype, all counters contiguous.
   L->off_part = off;
-  if (L->splits > 1) {
-    const int64_t ids = (int64_t)L->count[HC_GLOBAL] * g.q_tiles;
-    const size_t part = (size_t)ids * L->splits * qtile_of(c) * ((size_t)c->head_dim + 2) * sizeof(float);
-    L->off_counters = align256(off + part);
-    L->n_counters = ids;
-    off = align256(L->off_counters + ids * sizeof(int32_t));
-  } else {
-    L->off_counters = off;
+  for (int lab : {HC_GLOBAL, HC_SINK, HC_DUMMY}) {
+    if (L->splits[lab] == 1) continue;
+    const int64_t ids = (int64_t)L->count[lab] * g.q_tiles;
+    L->part_at[lab] = off;
+    off = align256(off + (size_t)ids * L->splits[lab] * qtile_of(c) * ((size_t)c->head_dim + 2) * sizeof(float));
   }
+  L->off_counters = off;
+  for (int lab : {HC_GLOBAL, HC_SINK, HC_DUMMY}) {
+    if (L->splits[lab] == 1) continue;
+    L->counter_at[lab] = L->n_counters;
+    L->n_counters += (int64_t)L->count[lab] * g.q_tiles;
+  }
+  off = align256(off + (size_t)L->n_counters * sizeof(int32_t));
   L->scratch_bytes = off - L->off_part;
   L->total = off;
   return HC_OK;
@@ -287,7 +306,9 @@ hc_status hc_cache_get_layout(const hc_cache* c, hc_cache_layout* out) {
   out->n_dummy = c->L.count[HC_DUMMY];
   out->n_spatial = c->L.count[HC_SPATIAL];
   out->blocks_appended = c->n_appended;
-  out->global_splits = c->L.splits;
+  out->global_splits = c->L.splits[HC_GLOBAL];
+  out->sink_splits = c->L.splits[HC_SINK];
+  out->dummy_splits = c->L.splits[HC_DUMMY];
   for (int h = 0; h < c->cfg.num_heads; ++h) out->head_slot[h] = c->L.slot[h];
   return HC_OK;
 }
@@ -307,7 +328,7 @@ hc_status hc_cache_append(hc_cache* c, hc_tensor k_block, hc_tensor v_block, int
   const int b = (mode == HC_PUSH_BLOCK) ? c->n_appended : c->n_appended - 1;
   const size_t e = elt_size(cfg->dtype);
 
-  if (c->L.splits > 1 && !c->counters_zeroed) {
+  if (c->L.n_counters > 0 && !c->counters_zeroed) {
     hipError_t err = launch_fill_zero((int32_t*)(c->dev + c->L.off_counters), c->L.n_counters, stream);
     if (err != hipSuccess) return hip_fail(err, "zeroing split counters");
     c->counters_zeroed = true;
@@ -405,13 +426,13 @@ hc_status hc_attend(hc_cache* c, hc_tensor q, hc_out_tensor out, hipStream_t str
       C.kv_first = 0;
       C.kv_count = (lab == HC_GLOBAL) ? nblk * g.Nq : g.Nq;
       C.keys_per_split = C.kv_count;
-      if (lab == HC_GLOBAL && c->L.splits > 1) {
+      if (c->L.splits[lab] > 1) {
         const int tiles = cdiv(C.kv_count, KTILE);
-        const int kps = cdiv(tiles, c->L.splits) * KTILE;
+        const int kps = cdiv(tiles, c->L.splits[lab]) * KTILE;
         C.keys_per_split = kps;
         C.splits = cdiv(C.kv_count, kps);
-        C.part = (float*)(c->dev + c->L.off_part);
-        C.counters = (int32_t*)(c->dev + c->L.off_counters);
+        C.part = (float*)(c->dev + c->L.part_at[lab]);
+        C.counters = (int32_t*)(c->dev + c->L.off_counters) + c->L.counter_at[lab];
       }
       C.units_per_head = g.q_tiles * C.splits;
     }

@@ -137,6 +137,18 @@ __device__ __forceinline__ Pair halves(float x) {
 // accumulator is rescaled on a few early tiles only.
 constexpr float kLazyLog2 = 8.0f;
 
+// Device-coherent 8-byte store / load (relaxed, agent scope: sc1), used for
+// the split partials that another XCD's work group merges.
+__device__ __forceinline__ void store_coherent(uint64_t* p, float a, float b) {
+  const uint64_t v = (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32);
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void load_coherent(const uint64_t* p, float& a, float& b) {
+  const uint64_t v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  a = __uint_as_float((uint32_t)v);
+  b = __uint_as_float((uint32_t)(v >> 32));
+}
+
 template <bool OUT_F32>
 __device__ __forceinline__ void store_row4(void* base, int64_t off, f32x4 v) {
   if constexpr (OUT_F32) {
@@ -169,8 +181,19 @@ void attn_bf16_kernel(const AttnPlan P) {
     if (c < P.n_cats && u >= P.cat[c].unit_begin) ci = c;
   const AttnCat& C = P.cat[ci];
   const int rel = u - C.unit_begin;
-  const int slot = rel / C.units_per_head;
-  const int j = rel - slot * C.units_per_head;
+  int slot, j;
+  if (C.kind == KIND_RANGED) {
+    slot = rel / C.units_per_head;
+    j = rel - slot * C.units_per_head;
+  } else {
+    // Spatial units go sub-tile by sub-tile over all heads and cells, so every
+    // cell's first (full) query sub-tile starts before any short remainder.
+    const int n_cells = C.units_per_head / P.cell_subtiles;
+    const int per_st = C.n_heads * n_cells;
+    const int st = rel / per_st, rem = rel - st * per_st;
+    slot = rem / n_cells;
+    j = (rem - slot * n_cells) * P.cell_subtiles + st;
+  }
   const int qh = P.head_of[ci][slot];
   const uint16_t* __restrict__ Kb = (const uint16_t*)C.k + slot * C.kv_sh;
   const uint16_t* __restrict__ Vb = (const uint16_t*)C.v + slot * C.kv_sh;
@@ -459,70 +482,79 @@ void attn_bf16_kernel(const AttnPlan P) {
   const int splits = ranged ? C.splits : 1;
 
   if (splits > 1) {
-    // Write this split's unnormalised partial; the last split to arrive merges.
+    // Write this split's unnormalised partial, count it, and let the last split
+    // to arrive merge.  The partials and the counter are accessed only with
+    // device-coherent (sc1) operations, which reach the memory side past the
+    // per-XCD L2s, so no fence has to write back or invalidate a whole L2.
+    // Partial layout per (id, split): O as [D/2][QT] float2 (consecutive
+    // queries adjacent), then (m, l) as [QT] float2 after all O planes.
     const int id = slot * P.q_tiles + tile;
     const int n_ids = C.n_heads * P.q_tiles;
-    float* po = C.part + ((int64_t)id * splits + split) * QT * D;
-    float* pml = C.part + (int64_t)n_ids * splits * QT * D + ((int64_t)id * splits + split) * QT * 2;
+    uint64_t* po = (uint64_t*)(C.part + ((int64_t)id * splits + split) * QT * D);
+    uint64_t* pml = (uint64_t*)(C.part + (int64_t)n_ids * splits * QT * D) + ((int64_t)id * splits + split) * QT;
     if (wave_active) {
 #pragma unroll
       for (int b = 0; b < QB; ++b) {
 #pragma unroll
         for (int t = 0; t < D / 32; ++t)
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            f32x4 w4 = {oacc[b][t][4 * g], oacc[b][t][4 * g + 1], oacc[b][t][4 * g + 2], oacc[b][t][4 * g + 3]};
-            *(f32x4*)(po + qlocal[b] * D + 32 * t + 8 * g + 4 * hi) = w4;
-          }
-        if (hi == 0) {
-          pml[2 * qlocal[b]] = m_run[b];
-          pml[2 * qlocal[b] + 1] = l_tot[b];
-        }
+          for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+              store_coherent(po + (int64_t)(2 * (8 * t + 2 * g + hi) + e) * QT + qlocal[b],
+                             oacc[b][t][4 * g + 2 * e], oacc[b][t][4 * g + 2 * e + 1]);
+        if (hi == 0) store_coherent(pml + qlocal[b], m_run[b], l_tot[b]);
       }
     }
-    __threadfence();
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this lane's stores have landed
     __syncthreads();
     if (tid == 0) {
-      const int old = atomicAdd(C.counters + id, 1);
+      const int old = __hip_atomic_fetch_add(C.counters + id, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       s_last = (old == splits - 1);
     }
     __syncthreads();
     if (!s_last) return;
-    __threadfence();
-    if (tid == 0) C.counters[id] = 0;   // ready for the next call
+    if (tid == 0) __hip_atomic_store(C.counters + id, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // next call
     // merge all splits for this lane's queries (its half of the channels)
-    const float* pml0 = C.part + (int64_t)n_ids * splits * QT * D + (int64_t)id * splits * QT * 2;
+    const uint64_t* pml0 = (const uint64_t*)(C.part + (int64_t)n_ids * splits * QT * D) + (int64_t)id * splits * QT;
 #pragma unroll
     for (int b = 0; b < QB; ++b) {
       if (!qvalid[b]) continue;
+      float ms[kMaxSplits], ls[kMaxSplits];
       float M = -INFINITY;
-      for (int s = 0; s < splits; ++s) M = fmaxf(M, pml0[s * QT * 2 + 2 * qlocal[b]]);
+#pragma unroll
+      for (int s = 0; s < kMaxSplits; ++s) {   // splits <= kMaxSplits; all loads issued together
+        load_coherent(pml0 + (int64_t)min(s, splits - 1) * QT + qlocal[b], ms[s], ls[s]);
+        if (s < splits) M = fmaxf(M, ms[s]);
+      }
       float L = 0.f;
-      f32x4 acc[D / 32][4];
+      float acc[D / 2];   // this lane's 16 (D=128) or 8 (D=64) column quadruples
 #pragma unroll
-      for (int t = 0; t < D / 32; ++t)
+      for (int i = 0; i < D / 2; ++i) acc[i] = 0.f;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) acc[t][g] = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int s = 0; s < splits; ++s) {
-        const float ms = pml0[s * QT * 2 + 2 * qlocal[b]];
-        const float ls = pml0[s * QT * 2 + 2 * qlocal[b] + 1];
-        const float w = __builtin_amdgcn_exp2f((ms - M) * c2);
-        L = fmaf(w, ls, L);
-        const float* ps = C.part + ((int64_t)id * splits + s) * QT * D + qlocal[b] * D;
+      for (int s = 0; s < kMaxSplits; ++s) {
+        if (s >= splits) break;   // uniform
+        const float w = __builtin_amdgcn_exp2f((ms[s] - M) * c2);
+        L = fmaf(w, ls[s], L);
+        const uint64_t* ps = (const uint64_t*)(C.part + ((int64_t)id * splits + s) * QT * D);
+        float x[D / 2];
 #pragma unroll
-        for (int t = 0; t < D / 32; ++t)
+        for (int i = 0; i < D / 4; ++i)   // i = 2*(4t+g)+e
+          load_coherent(ps + (int64_t)(2 * (8 * (i >> 3) + 2 * ((i >> 1) & 3) + hi) + (i & 1)) * QT + qlocal[b],
+                        x[2 * i], x[2 * i + 1]);
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const f32x4 x = *(const f32x4*)(ps + 32 * t + 8 * g + 4 * hi);
-            acc[t][g] += w * x;
-          }
+        for (int i = 0; i < D / 2; ++i) acc[i] = fmaf(w, x[i], acc[i]);
       }
       const float inv = 1.f / L;
       const int64_t obase = (int64_t)qh * C.o_sh + (int64_t)qtok[b] * C.o_st;
 #pragma unroll
       for (int t = 0; t < D / 32; ++t)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) store_row4<OUT_F32>(C.o, obase + 32 * t + 8 * g + 4 * hi, acc[t][g] * inv);
+        for (int g = 0; g < 4; ++g) {
+          const int i = 4 * (4 * t + g);
+          const f32x4 v = {acc[i] * inv, acc[i + 1] * inv, acc[i + 2] * inv, acc[i + 3] * inv};
+          store_row4<OUT_F32>(C.o, obase + 32 * t + 8 * g + 4 * hi, v);
+        }
     }
     return;
   }

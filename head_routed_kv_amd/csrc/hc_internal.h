@@ -18,10 +18,12 @@ namespace hc {
 //                rows [W*off_c, W*off_c + nf*|c|);
 //   CELL_GATHER  Spatial pathway over a frame-major window: the keys of cell c
 //                in frames 0..nf-1 are gathered row by row.
-// Units are numbered category by category (heaviest first), head by head.
-// Ranged units are (split, q-tile) pairs, split-major, so that work groups
-// running at the same time on one XCD share the same key rows in L2.  Spatial
-// units are (cell, q-sub-tile) pairs; sub-tiles past a small cell are empty.
+// Units are numbered category by category (heaviest first).  Ranged units are
+// (head, split, q-tile), q-tile fastest, so that work groups running at the
+// same time read the same key rows.  Spatial units are (head, cell, q-sub-tile)
+// in the fp32 kernel and (q-sub-tile, head, cell) in the bf16 kernel, whose
+// cells' full first sub-tiles thus start before the short remainders;
+// sub-tiles past a small cell are empty.
 // ---------------------------------------------------------------------------
 enum : int32_t { KIND_RANGED = 0, KIND_CELL_MAJOR = 1, KIND_CELL_GATHER = 2 };
 
@@ -31,6 +33,7 @@ constexpr int kBf16GroupsPerCU = 8 / (kBf16Waves * kBf16QueryBlocks);  // 2 wave
 constexpr int QTILE_BF16 = 32 * kBf16QueryBlocks * kBf16Waves;          // queries per work group, bf16 kernel
 constexpr int QTILE_F32 = 128;                       // queries per work group, fp32 kernel
 constexpr int KTILE = 64;                            // keys per inner iteration
+constexpr int kMaxSplits = 8;                        // key-range splits per ranged head, at most
 
 struct AttnCat {
   int32_t kind;
@@ -46,7 +49,7 @@ struct AttnCat {
   int64_t kv_sh, kv_st;   // slot (head) stride and token stride, elements
   void* o;                // output base for this category
   int64_t o_sh, o_st;     // output head / token strides, elements
-  float* part;            // split partials: [tile_id][splits][q tile][D] fp32, then (m,l) pairs
+  float* part;            // split partials: O as [id][split][D/2][q tile] float2, then (m,l) as [id][split][q tile] float2
   int32_t* counters;      // one per (head slot, q tile) when splits > 1
   int32_t out_f32;        // output written as fp32 (else the input dtype)
   int32_t pad_;

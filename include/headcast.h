@@ -133,7 +133,9 @@ typedef struct hc_cache_layout {
   uint64_t off_scratch, scratch_bytes;
   int32_t n_global, n_sink, n_dummy, n_spatial;
   int32_t blocks_appended;
-  int32_t global_splits; /* key-range splits used for Global heads by hc_attend */
+  /* key-range splits hc_attend uses for the Global, Sink and Dummy heads
+   * (chosen from the layer shape so that the work units fill the GPU) */
+  int32_t global_splits, sink_splits, dummy_splits;
   int32_t head_slot[HC_MAX_HEADS];
 } hc_cache_layout;
 

@@ -151,3 +151,15 @@ def test_split_plan_for_benchmark_layers():
     h = N.hc_cache_create(cfg(), [0, 1, 2, 3], FAKE, N.hc_cache_bytes(cfg(), [0, 1, 2, 3]))
     assert N.hc_cache_get_layout(h).global_splits == 1
     N.hc_cache_destroy(h)
+    # two Sink heads alone: 2 x 43 q tiles; their key sets are split as well
+    c = N.make_config(2, 128, 45, 80, 3, 21)
+    h = N.hc_cache_create(c, [0, 0], FAKE, N.hc_cache_bytes(c, [0, 0]))
+    lay = N.hc_cache_get_layout(h)
+    assert lay.sink_splits > 1 and lay.global_splits == 1 and lay.scratch_bytes > 0
+    N.hc_cache_destroy(h)
+    # fp32 layers are never split
+    c = N.make_config(2, 128, 45, 80, 3, 21, dtype=N.HC_FP32)
+    h = N.hc_cache_create(c, [0, 3], FAKE, N.hc_cache_bytes(c, [0, 3]))
+    lay = N.hc_cache_get_layout(h)
+    assert (lay.global_splits, lay.sink_splits, lay.dummy_splits, lay.scratch_bytes) == (1, 1, 1, 0)
+    N.hc_cache_destroy(h)

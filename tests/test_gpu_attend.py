@@ -60,6 +60,21 @@ def test_global_key_splits_merge():
     assert torch().equal(out, out2)
 
 
+def test_sink_dummy_key_splits_merge():
+    """Sink and Dummy heads alone cannot fill the GPU: the cache splits their
+    key sets too and the kernel merges the partials per category."""
+    wl = W.Workload("sdsplit", 13, 4, 128, 16, 16, 4, 8, "bf16", "uniform")
+    labels = [0, 1, 1, 0]
+    say("case sink/dummy split merge")
+    data, cache, out = run_window(wl, labels, seed=8)
+    lay = cache.layout()
+    assert lay.sink_splits > 1 and lay.dummy_splits > 1 and lay.global_splits == 1
+    check_close(to_float(out), oracle_routed(wl, data, labels), BF16_TOL, "sink/dummy split")
+    out2 = cache.attend(upload(data["q"], wl))
+    torch().cuda.synchronize()
+    assert torch().equal(out, out2)
+
+
 def test_fp32_spatial_and_global_small():
     wl = W.Workload("small32", 11, 4, 128, 13, 21, 2, 6, "fp32", "uniform")
     labels = [2, 3, 1, 0]
