@@ -114,6 +114,80 @@ def make_flush(device):
     return flush
 
 
+def rollout_costs(wl, labels, q, k, v, full_ms, steps_per_block=4, lengths=(14, 40)):
+    """Attention cost of one layer over a video rollout, phase by phase.
+
+    Warm-up: while the first window fills, every head attends over the growing
+    window (each block: one push and steps_per_block - 1 replacements, an
+    attend after each).  At first fill: hc_classify on the window, then the
+    window's blocks are replayed into the routed cache.  Afterwards each block's
+    steps go through the routed cache.  The routed cache uses this layer's
+    label mix (the classifier runs on the same random inputs only for its
+    time).  Routed blocks are timed over 8 blocks; longer rollouts are
+    extrapolated from that steady-state cost."""
+    import torch
+    import head_routed_kv_amd as hk
+    from head_routed_kv_amd.session import LayerSession
+    nb, BT = wl.window_frames // wl.block_frames, wl.Nq
+    cfg = hk.make_config(wl.heads, wl.head_dim, wl.grid_h, wl.grid_w, wl.block_frames, wl.window_frames)
+    out = torch.empty_like(q)
+
+    def timed(fn):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        b.synchronize()
+        return a.elapsed_time(b)
+
+    def blk(kk, vv, b):
+        return kk[:, b * BT:(b + 1) * BT], vv[:, b * BT:(b + 1) * BT]
+
+    sess = LayerSession(cfg)
+    ws = hk.classify(cfg, q, k, v)[2]          # workspace, allocated outside the timed region
+    torch.cuda.synchronize()
+
+    def block_steps(cache_push, cache_replace, attend, kb, vb):
+        for s in range(steps_per_block):
+            (cache_push if s == 0 else cache_replace)(kb, vb)
+            attend(q, out)
+
+    warm_ms = sum(timed(lambda b=b: block_steps(sess.push, sess.replace, sess.attend, *blk(k, v, b)))
+                  for b in range(nb))
+    kw, vw = sess.window_views()
+    cls_ms = timed(lambda: hk.classify(cfg, q, kw, vw, workspace=ws))
+    holder = {}
+
+    def restructure():
+        holder["c"] = hk.RoutedCache(cfg, [int(x) for x in labels])
+        for b in range(nb):
+            holder["c"].append(*blk(kw, vw, b))
+    rest_ms = timed(restructure)
+    routed = holder["c"]
+    rep = lambda kb, vb: routed.append(kb, vb, hk.HC_REPLACE_NEWEST)
+    n_timed = 8
+    routed_ms = sum(timed(lambda b=b: block_steps(routed.append, rep, routed.attend, *blk(k, v, b % nb)))
+                    for b in range(n_timed)) / n_timed
+    sess.close()
+    routed.close()
+    full_block_ms = full_ms * steps_per_block
+    res = {"steps_per_block": steps_per_block, "warmup_ms": round(warm_ms, 2), "classify_ms": round(cls_ms, 3),
+           "restructure_ms": round(rest_ms, 3), "routed_block_ms": round(routed_ms, 3),
+           "full_block_ms": round(full_block_ms, 3), "by_blocks": {}}
+    for n in lengths:
+        total = warm_ms + cls_ms + rest_ms + (n - nb) * routed_ms
+        full_total = warm_ms + (n - nb) * full_block_ms
+        res["by_blocks"][str(n)] = {"attention_ms": round(total, 1),
+                                    "classification_share": round((cls_ms + rest_ms) / total, 4),
+                                    "speedup_vs_full_attention": round(full_total / total, 3)}
+    return res
+
+
+def box_span(n, r):
+    """Sum over positions 0..n-1 of the box extent [p-r, p+r] cut to [0, n)."""
+    return sum(min(p + r, n - 1) - max(p - r, 0) + 1 for p in range(n))
+
+
 def counter_traffic(workload):
     """HBM bytes per launch of the attention kernel from the committed
     rocprofv3 FETCH_SIZE / WRITE_SIZE record, scaled by its copy calibration.
@@ -251,6 +325,7 @@ def main():
                            "tflops": round(f / (ms / 1e3) / 1e12, 1), "mfma_frac": round(f / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                            "hbm_gbs": round(by / (ms / 1e3) / 1e9, 1), "hbm_frac": round(by / (ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4)}
             del lay
+        extra["rollout"] = rollout_costs(wl, labels, q, k, v, full_ms)
         del layer, q, k, v
         torch.cuda.empty_cache()
         # 1080p layer
@@ -282,6 +357,18 @@ def main():
         f3 = wl3.heads * 4 * wl3.head_dim * pairs
         extra["classifier720p"] = {"heads": wl3.heads, "ms": round(cls_ms, 3), "tflops": round(f3 / (cls_ms / 1e3) / 1e12, 1),
                                    "mfma_frac": round(f3 / (cls_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        # the same with the pages' sliding 5x5 box as the Spatial proxy
+        pb = hk.hc_default_classify_params()
+        pb.spatial_proxy, pb.radius = 1, 2
+        for _ in range(2):
+            hk.classify(cfg3, q3, k3, v3, pb, workspace=ws)
+        box_ms = time_events(lambda: hk.classify(cfg3, q3, k3, v3, pb, workspace=ws), 3)
+        pairs_b = wl3.Nq * wl3.Nk + 2 * wl3.Nq * BT + \
+            wl3.block_frames * wl3.window_frames * box_span(wl3.grid_h, 2) * box_span(wl3.grid_w, 2)
+        fb = wl3.heads * 4 * wl3.head_dim * pairs_b
+        extra["classifier720p_box"] = {"heads": wl3.heads, "ms": round(box_ms, 3),
+                                       "tflops": round(fb / (box_ms / 1e3) / 1e12, 1),
+                                       "mfma_frac": round(fb / (box_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
         del q3, k3, v3, ws
 
     cpu = None

@@ -464,8 +464,9 @@ hc_status hc_classify(const hc_config* cfg, const hc_classify_params* prm, hc_te
   if (st) return st;
   if (!prm) return fail(HC_ERR_INVALID_ARG, "params is NULL");
   if (prm->rule != 0 && prm->rule != 1) return fail(HC_ERR_INVALID_ARG, "rule %d", prm->rule);
-  if (prm->spatial_proxy == 1) return fail(HC_ERR_UNSUPPORTED, "the sliding-box Spatial proxy is not implemented");
-  if (prm->spatial_proxy != 0) return fail(HC_ERR_INVALID_ARG, "spatial_proxy %d", prm->spatial_proxy);
+  if (prm->spatial_proxy != 0 && prm->spatial_proxy != 1) return fail(HC_ERR_INVALID_ARG, "spatial_proxy %d", prm->spatial_proxy);
+  if (prm->spatial_proxy == 1 && (prm->radius < 0 || prm->radius > kMaxBoxRadius))
+    return fail(HC_ERR_INVALID_ARG, "radius %d outside 0..%d", prm->radius, kMaxBoxRadius);
   if (!(prm->percentile >= 0.f && prm->percentile <= 100.f)) return fail(HC_ERR_INVALID_ARG, "percentile outside 0..100");
   if (!std::isfinite(prm->gamma)) return fail(HC_ERR_INVALID_ARG, "gamma is not finite");
   if ((st = check_tensor(q.ptr, q.stride_head, q.stride_token, cfg, "q_block"))) return st;
@@ -526,10 +527,21 @@ hc_status hc_classify(const hc_config* cfg, const hc_classify_params* prm, hc_te
       C.kv_count = count[k];
       C.keys_per_split = count[k];
       C.units_per_head = g.q_tiles;
-    } else {
+    } else if (prm->spatial_proxy == 0) {
       C.kind = KIND_CELL_GATHER;
       C.kv_count = cfg->window_frames;
       C.units_per_head = g.n_cells * g.cell_subtiles;
+    } else {
+      // sliding (2r+1)^2 box: patches of (queries per work group / 32) rows x
+      // (32 - 2r) columns, so each patch's key rows are 32 columns wide
+      C.kind = KIND_BOX_GATHER;
+      C.kv_count = cfg->window_frames;
+      P.box_r = prm->radius;
+      P.box_rows = (cfg->dtype == HC_BF16 ? QTILE_BF16 : QTILE_F32) / 32;
+      P.box_cols_q = 32 - 2 * prm->radius;
+      P.box_bands_y = cdiv(cfg->grid_h, P.box_rows);
+      P.box_bands_x = cdiv(cfg->grid_w, P.box_cols_q);
+      C.units_per_head = cfg->block_frames * P.box_bands_y * P.box_bands_x;
     }
     for (int h = 0; h < H; ++h) P.head_of[k][h] = (uint8_t)h;
     units += H * C.units_per_head;

@@ -123,6 +123,10 @@ __device__ __forceinline__ int cell_token(const AttnPlan& P, const CellInfo& c, 
   return f * P.T + c.base + ry * P.grid_w + (r - ry * c.width);
 }
 
+// Initial running max: finite, so that a tile whose keys are all masked for a
+// query (box proxy) gives exp2(-inf) = 0 instead of exp2(-inf + inf) = NaN.
+constexpr float kNoMax = -1e30f;
+
 // Values of lanes l and l^32 (in either order), via v_permlane32_swap.
 struct Pair {
   float a, b;
@@ -182,7 +186,7 @@ void attn_bf16_kernel(const AttnPlan P) {
   const AttnCat& C = P.cat[ci];
   const int rel = u - C.unit_begin;
   int slot, j;
-  if (C.kind == KIND_RANGED) {
+  if (C.kind == KIND_RANGED || C.kind == KIND_BOX_GATHER) {
     slot = rel / C.units_per_head;
     j = rel - slot * C.units_per_head;
   } else {
@@ -202,7 +206,9 @@ void attn_bf16_kernel(const AttnPlan P) {
   // ---- what this unit covers --------------------------------------------
   int q0, qn, k0, kn, split = 0, tile = 0;
   CellInfo cell = {0, 0, 1, 0};
+  BoxInfo box = {0, 0, 0};
   const bool ranged = (C.kind == KIND_RANGED);
+  const bool is_box = GATHER && C.kind == KIND_BOX_GATHER;
   if (ranged) {
     split = j / P.q_tiles;
     tile = j - split * P.q_tiles;
@@ -210,6 +216,12 @@ void attn_bf16_kernel(const AttnPlan P) {
     qn = min(QT, P.Nq - q0);
     k0 = C.kv_first + split * C.keys_per_split;
     kn = min(C.keys_per_split, C.kv_count - split * C.keys_per_split);
+  } else if (is_box) {
+    box = box_info(P, j);
+    q0 = 0;
+    qn = QT;   // query validity is decided per lane from the patch
+    kn = C.kv_count * (P.box_rows + 2 * P.box_r) * 32;
+    k0 = 0;
   } else {
     const int c = j / P.cell_subtiles;
     const int st = j - c * P.cell_subtiles;
@@ -235,9 +247,15 @@ void attn_bf16_kernel(const AttnPlan P) {
 #pragma unroll
   for (int b = 0; b < QB; ++b) {
     qlocal[b] = wave * 32 * QB + 32 * b + l32;
-    qvalid[b] = qlocal[b] < qn;
     qtok[b] = 0;
-    if (qvalid[b]) qtok[b] = ranged ? (q0 + qlocal[b]) : cell_token(P, cell, q0 + qlocal[b]);
+    if (is_box) {   // patch row wave*QB+b, column l32
+      const int y = box.py0 + wave * QB + b, x = box.px0 + l32;
+      qvalid[b] = l32 < P.box_cols_q && y < P.grid_h && x < P.grid_w;
+      if (qvalid[b]) qtok[b] = box.fb * P.T + y * P.grid_w + x;
+    } else {
+      qvalid[b] = qlocal[b] < qn;
+      if (qvalid[b]) qtok[b] = ranged ? (q0 + qlocal[b]) : cell_token(P, cell, q0 + qlocal[b]);
+    }
     const uint16_t* qrow = Qb + (int64_t)qtok[b] * P.q_st + 8 * hi;
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
@@ -246,7 +264,19 @@ void attn_bf16_kernel(const AttnPlan P) {
       qb[b][s] = __builtin_bit_cast(bf16x8, w);
     }
   }
-  const bool wave_active = wave * 32 * QB < qn;
+  const bool wave_active = is_box ? (box.py0 + wave * QB < P.grid_h) : (wave * 32 * QB < qn);
+  // Box proxy: bit rx of box_cm says whether this lane's query may see box
+  // column rx (within r columns of it, and on the grid), shifted so that bit
+  // 8a+e stands for column 8a+4*hi+e, the keys this lane's score registers hold.
+  uint32_t box_cm = 0;
+  if (is_box) {
+    uint32_t m = ((1u << (2 * P.box_r + 1)) - 1u) << l32;
+    const int rx_min = P.box_r - box.px0;                  // first on-grid column
+    const int rx_max = P.grid_w - 1 - box.px0 + P.box_r;   // last on-grid column (>= r)
+    if (rx_min > 0) m &= ~((1u << rx_min) - 1u);
+    if (rx_max < 31) m &= (2u << rx_max) - 1u;
+    box_cm = m >> (4 * hi);
+  }
   // Q has landed (vmcnt(0); expcnt and lgkmcnt untouched).  Said once here, in
   // the form the compiler's wait bookkeeping understands, so the tile loop
   // never waits for Q again.
@@ -292,7 +322,8 @@ void attn_bf16_kernel(const AttnPlan P) {
       for (int i = 0; i < TL::LPW; ++i) {
         const int r = TL::RPI * (NW * i + wave) + lane / TL::CPR;
         const int slot_c = lane % TL::CPR;
-        const int64_t row = (int64_t)cell_token(P, cell, lb + lrow[i]) * rowb;
+        const int tok = is_box ? box_token(P, box, lb + lrow[i]) : cell_token(P, cell, lb + lrow[i]);
+        const int64_t row = (int64_t)tok * rowb;
         lds_dma16_addr(Kc + row + 16 * (slot_c ^ swz_k<D>(r)), kdst + 1024 * (NW * i + wave));
         lds_dma16_addr(Vc + row + 16 * (slot_c ^ swz_v<D>(r)), vdst + 1024 * (NW * i + wave));
       }
@@ -313,7 +344,7 @@ void attn_bf16_kernel(const AttnPlan P) {
   f32x16 oacc[QB][D / 32];
 #pragma unroll
   for (int b = 0; b < QB; ++b) {
-    m_run[b] = -INFINITY;
+    m_run[b] = kNoMax;
     l_run[b] = 0.f;
 #pragma unroll
     for (int t = 0; t < D / 32; ++t) oacc[b][t] = f32x16{};
@@ -384,6 +415,23 @@ void attn_bf16_kernel(const AttnPlan P) {
           for (int b = 0; b < QB; ++b) {
             if (key < lo || key >= hi_end) sc[b][0][jj] = -INFINITY;
             if (key + 32 < lo || key + 32 >= hi_end) sc[b][1][jj] = -INFINITY;
+          }
+        }
+      }
+      if constexpr (GATHER) {
+        if (is_box) {   // box proxy: only keys within r rows and r columns count
+          const int rows = P.box_rows + 2 * P.box_r;
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            const int ky = box.py0 - P.box_r + (2 * it + c) % rows;   // uniform
+#pragma unroll
+            for (int b = 0; b < QB; ++b) {
+              const int qy = box.py0 + wave * QB + b;
+              const bool row_ok = ky >= 0 && ky < P.grid_h && abs(ky - qy) <= P.box_r;
+#pragma unroll
+              for (int jj = 0; jj < 16; ++jj)
+                if (!row_ok || !((box_cm >> (8 * (jj >> 2) + (jj & 3))) & 1u)) sc[b][c][jj] = -INFINITY;
+            }
           }
         }
       }
@@ -580,9 +628,10 @@ void attn_bf16_kernel(const AttnPlan P) {
 hipError_t launch_attn_bf16(const AttnPlan& plan, int head_dim, hipStream_t s) {
   if (plan.total_units <= 0) return hipSuccess;
   const bool f32 = plan.cat[0].out_f32 != 0;
-  const bool gather = plan.cat[0].kind == KIND_CELL_GATHER;
+  auto gathers = [](int kind) { return kind == KIND_CELL_GATHER || kind == KIND_BOX_GATHER; };
+  const bool gather = gathers(plan.cat[0].kind);
   for (int c = 1; c < plan.n_cats; ++c)
-    if ((plan.cat[c].kind == KIND_CELL_GATHER) != gather) return hipErrorInvalidValue;  // one mode per launch
+    if (gathers(plan.cat[c].kind) != gather) return hipErrorInvalidValue;  // one mode per launch
   dim3 grid(plan.total_units), block(NT);
 #define HC_LAUNCH(DD, F, G) hipLaunchKernelGGL((attn_bf16_kernel<DD, kBf16QueryBlocks, F, G>), grid, block, 0, s, plan)
   if (head_dim == 128) {

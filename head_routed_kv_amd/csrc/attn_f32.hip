@@ -55,7 +55,9 @@ __global__ __launch_bounds__(NT) void attn_f32_kernel(const AttnPlan P) {
 
   int q0, qn, k0, kn;
   CellInfo cell = {0, 0, 1, 0};
+  BoxInfo box = {0, 0, 0};
   const bool ranged = C.kind == KIND_RANGED;
+  const bool is_box = C.kind == KIND_BOX_GATHER;
   if (ranged) {
     const int split = j / P.q_tiles;
     const int tile = j - split * P.q_tiles;
@@ -64,6 +66,12 @@ __global__ __launch_bounds__(NT) void attn_f32_kernel(const AttnPlan P) {
     k0 = C.kv_first;
     kn = C.kv_count;   // this kernel never splits the key range
     (void)split;
+  } else if (is_box) {
+    box = box_info(P, j);
+    q0 = 0;
+    qn = QTILE_F32;
+    kn = C.kv_count * (P.box_rows + 2 * P.box_r) * 32;
+    k0 = 0;
   } else {
     const int c = j / P.cell_subtiles;
     const int st = j - c * P.cell_subtiles;
@@ -75,13 +83,15 @@ __global__ __launch_bounds__(NT) void attn_f32_kernel(const AttnPlan P) {
     kn = C.kv_count * cell.size;
     k0 = (C.kind == KIND_CELL_MAJOR) ? P.W * cell.off : 0;
   }
-  const bool gather = C.kind == KIND_CELL_GATHER;
+  const bool gather = C.kind == KIND_CELL_GATHER || is_box;
 
   const int tid = threadIdx.x;
   const int ql = tid >> 1, half = tid & 1;
-  const bool qvalid = ql < qn;
+  // box proxy: query ql is patch row ql / 32, column ql % 32
+  const int qy = box.py0 + (ql >> 5), qx = box.px0 + (ql & 31);
+  const bool qvalid = is_box ? ((ql & 31) < P.box_cols_q && qy < P.grid_h && qx < P.grid_w) : ql < qn;
   int qtok = 0;
-  if (qvalid) qtok = ranged ? q0 + ql : cell_token(P, cell, q0 + ql);
+  if (qvalid) qtok = is_box ? box.fb * P.T + qy * P.grid_w + qx : ranged ? q0 + ql : cell_token(P, cell, q0 + ql);
   float q[H2], o[H2];
 #pragma unroll
   for (int c = 0; c < H2; ++c) {
@@ -99,7 +109,8 @@ __global__ __launch_bounds__(NT) void attn_f32_kernel(const AttnPlan P) {
       const int kk = kb + r;
       f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
       if (kk < kn) {
-        const int64_t row = gather ? (int64_t)cell_token(P, cell, kk) : (int64_t)(k0 + kk);
+        const int64_t row = is_box ? (int64_t)box_token(P, box, kk)
+                            : gather ? (int64_t)cell_token(P, cell, kk) : (int64_t)(k0 + kk);
         a = *(const f32x4*)(Kb + row * C.kv_st + 4 * ch);
         b = *(const f32x4*)(Vb + row * C.kv_st + 4 * ch);
       }
@@ -109,6 +120,13 @@ __global__ __launch_bounds__(NT) void attn_f32_kernel(const AttnPlan P) {
     __syncthreads();
     const int nk = min(FKT, kn - kb);
     for (int r = 0; r < nk; ++r) {
+      if (is_box) {   // only keys within r rows and r columns of the query, on the grid
+        int f, ky, kx;
+        box_pos(P, box, kb + r, f, ky, kx);
+        const bool ok = ky >= 0 && ky < P.grid_h && kx >= 0 && kx < P.grid_w && abs(ky - qy) <= P.box_r &&
+                        abs(kx - qx) <= P.box_r;
+        if (!ok) continue;   // the same for both lanes of a query pair
+      }
       float dot = 0.f;
 #pragma unroll
       for (int c = 0; c < H2; ++c) dot = fmaf(q[c], Ks[r][half * H2 + c], dot);

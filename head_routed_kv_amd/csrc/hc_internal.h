@@ -25,7 +25,14 @@ namespace hc {
 // cells' full first sub-tiles thus start before the short remainders;
 // sub-tiles past a small cell are empty.
 // ---------------------------------------------------------------------------
-enum : int32_t { KIND_RANGED = 0, KIND_CELL_MAJOR = 1, KIND_CELL_GATHER = 2 };
+//   BOX_GATHER   classifier's sliding-box Spatial proxy over a frame-major
+//                window: a unit is a patch of box_rows x box_cols_q queries of
+//                one block frame; its keys are the (box_rows + 2r) x 32 grid
+//                positions around the patch (columns px0-r .. px0-r+31) in each
+//                of kv_count frames, frame by frame, row by row.  Positions off
+//                the grid are loaded clamped and masked; each query keeps only
+//                keys within r rows and r columns of itself.
+enum : int32_t { KIND_RANGED = 0, KIND_CELL_MAJOR = 1, KIND_CELL_GATHER = 2, KIND_BOX_GATHER = 3 };
 
 constexpr int kBf16QueryBlocks = 1;                  // 32-query blocks per wave, bf16 kernel
 constexpr int kBf16Waves = 8;                        // waves per work group, bf16 kernel
@@ -34,6 +41,7 @@ constexpr int QTILE_BF16 = 32 * kBf16QueryBlocks * kBf16Waves;          // queri
 constexpr int QTILE_F32 = 128;                       // queries per work group, fp32 kernel
 constexpr int KTILE = 64;                            // keys per inner iteration
 constexpr int kMaxSplits = 8;                        // key-range splits per ranged head, at most
+constexpr int kMaxBoxRadius = 8;                     // sliding-box proxy radius, at most (patches >= 16 columns)
 
 struct AttnCat {
   int32_t kind;
@@ -66,9 +74,43 @@ struct AttnPlan {
   // geometry
   int32_t T, grid_w, grid_h, cell_h, cell_w, cell_cols, B, W, Nq;
   float scale_log2;        // softmax scale * log2(e)
+  // sliding-box proxy (KIND_BOX_GATHER): radius, patch rows and columns,
+  // patches per frame down and across
+  int32_t box_r, box_rows, box_cols_q, box_bands_y, box_bands_x;
   AttnCat cat[4];
   uint8_t head_of[4][HC_MAX_HEADS];  // category slot -> q/o head index
 };
+
+// Patch of a KIND_BOX_GATHER unit: block frame, first query row and column.
+struct BoxInfo {
+  int fb, py0, px0;
+};
+__device__ __forceinline__ BoxInfo box_info(const AttnPlan& P, int j) {
+  const int per_frame = P.box_bands_y * P.box_bands_x;
+  BoxInfo b;
+  b.fb = j / per_frame;
+  const int rem = j - b.fb * per_frame;
+  const int by = rem / P.box_bands_x;
+  b.py0 = by * P.box_rows;
+  b.px0 = (rem - by * P.box_bands_x) * P.box_cols_q;
+  return b;
+}
+// Grid row and column of box key k (may lie off the grid).
+__device__ __forceinline__ void box_pos(const AttnPlan& P, const BoxInfo& b, int k, int& f, int& ky, int& kx) {
+  const int rows = P.box_rows + 2 * P.box_r;
+  const int rg = k >> 5;
+  f = rg / rows;
+  ky = b.py0 - P.box_r + (rg - f * rows);
+  kx = b.px0 - P.box_r + (k & 31);
+}
+// Window token loaded for box key k: its position clamped into the grid.
+__device__ __forceinline__ int box_token(const AttnPlan& P, const BoxInfo& b, int k) {
+  int f, ky, kx;
+  box_pos(P, b, k, f, ky, kx);
+  ky = min(max(ky, 0), P.grid_h - 1);
+  kx = min(max(kx, 0), P.grid_w - 1);
+  return f * P.T + ky * P.grid_w + kx;
+}
 
 // Launchers (return hipSuccess or the launch error).
 hipError_t launch_attn_bf16(const AttnPlan& plan, int head_dim, hipStream_t s);

@@ -102,8 +102,14 @@ typedef struct hc_out_tensor {
  *   rule           0: among the proxies that clear their thresholds pick the
  *                  one with the largest mean cosine (ties Sink<Dummy<Spatial);
  *                  1: the first that clears, in the order Sink, Dummy, Spatial
- *   spatial_proxy  0: the deployed grid cell; 1 is reserved for the
- *                  (2r+1)^2 sliding box and returns HC_ERR_UNSUPPORTED
+ *   spatial_proxy  0: the deployed grid cell (the query's 10x10 cell in every
+ *                  window frame); 1: the sliding (2r+1)^2 box the review says
+ *                  the paper classifies with ([Pith] Referee Report, comment
+ *                  2; ledger "Spatial proxy radius r = 2"): keys within
+ *                  `radius` rows and columns of the query, in every window
+ *                  frame, cut at the frame border
+ *   radius         box radius r for spatial_proxy 1, 0..8 (else
+ *                  HC_ERR_INVALID_ARG)
  *   percentile     rank of the worst-case Spatial cosine (5 = 5th percentile,
  *                  linear interpolation at rank p/100*(Nq-1)) */
 typedef struct hc_classify_params {

@@ -1,9 +1,11 @@
 """Write the oracle's expected labels and diagnostics for the planted
-classifier workload (40 heads at the 720p shape, seed 0).
+classifier workload (40 heads at the 720p shape, seed 0), with the deployed
+grid-cell Spatial proxy (default) or the sliding (2r+1)^2 box proxy
+(--spatial-proxy 1, file suffix _box).
 
 Calls only the CPU oracle and the seeded input generator.  Run from the
 repository root:  python tests/golden/make_classifier_golden.py [--procs N]
-Takes a few minutes on 8 cores."""
+[--spatial-proxy 1 --radius 2].  Takes about 45 minutes on 6 cores."""
 import argparse
 import json
 import os
@@ -18,15 +20,17 @@ os.environ.setdefault("OPENBLAS_NUM_THREADS", "1")
 
 
 def one_head(args):
-    name, seed, h = args
+    name, seed, h, proxy, radius = args
     from head_routed_kv_amd import workloads as W
     from oracle import headcast_oracle as O
     wl = W.WORKLOADS[name]
     data = W.window(wl, seed=seed, heads=[h], threads=1)
     q, k, v = (W.as_float(data[n], wl)[0] for n in ("q", "k", "v"))
     g = O.Geometry(wl.grid_h, wl.grid_w, wl.block_frames, wl.window_frames)
-    lab, diag, cos, mse = O.classify_head(q, k, v, g)
-    return h, int(lab), [float(x) for x in diag], float(mse), float(O.decision_margin(diag)), int(data["labels"][h])
+    prm = O.ClassifyParams(spatial_proxy=proxy, radius=radius)
+    lab, diag, cos, mse = O.classify_head(q, k, v, g, prm)
+    return h, int(lab), [float(x) for x in diag], float(mse), float(O.decision_margin(diag, prm)), \
+        int(data["labels"][h])
 
 
 def main():
@@ -34,19 +38,22 @@ def main():
     ap.add_argument("--workload", default="classifier720p")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--procs", type=int, default=6)
+    ap.add_argument("--spatial-proxy", type=int, default=0, choices=(0, 1))
+    ap.add_argument("--radius", type=int, default=2)
     a = ap.parse_args()
     from head_routed_kv_amd import workloads as W
     wl = W.WORKLOADS[a.workload]
     t0 = time.time()
     rows = {}
     with ProcessPoolExecutor(a.procs) as ex:
-        for h, lab, diag, mse, margin, planted in ex.map(one_head, [(a.workload, a.seed, h) for h in range(wl.heads)]):
+        for h, lab, diag, mse, margin, planted in ex.map(one_head, [(a.workload, a.seed, h, a.spatial_proxy, a.radius)
+                                                                       for h in range(wl.heads)]):
             rows[h] = dict(label=lab, diag=diag, mse=mse, margin=margin, planted=planted)
             print(f"head {h}: label {lab} planted {planted} diag {diag} margin {margin:.4f}", flush=True)
     out = {
         "_source": "CPU oracle (oracle/headcast_oracle.py, fp64) on the seeded planted workload; "
                    "written by tests/golden/make_classifier_golden.py",
-        "workload": a.workload, "seed": a.seed,
+        "workload": a.workload, "seed": a.seed, "spatial_proxy": a.spatial_proxy, "radius": a.radius,
         "labels": [rows[h]["label"] for h in range(wl.heads)],
         "planted": [rows[h]["planted"] for h in range(wl.heads)],
         "diag": [rows[h]["diag"] for h in range(wl.heads)],
@@ -54,7 +61,8 @@ def main():
         "margin": [rows[h]["margin"] for h in range(wl.heads)],
         "seconds": round(time.time() - t0, 1),
     }
-    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), f"{a.workload}_seed{a.seed}.json")
+    suffix = "" if a.spatial_proxy == 0 else ("_box" if a.radius == 2 else f"_box_r{a.radius}")
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), f"{a.workload}{suffix}_seed{a.seed}.json")
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
     print("wrote", path, "in", out["seconds"], "s")

@@ -129,8 +129,12 @@ def test_classify_argument_checks():
     assert L.hc_classify(*args(p, FAKE, need - 1)) == N.HC_ERR_WORKSPACE
     assert L.hc_classify(*args(p, FAKE + 16, need)) == N.HC_ERR_ALIGN
     p2 = N.hc_default_classify_params()
-    p2.spatial_proxy = 1
-    assert L.hc_classify(*args(p2, FAKE, need)) == N.HC_ERR_UNSUPPORTED
+    p2.spatial_proxy = 2
+    assert L.hc_classify(*args(p2, FAKE, need)) == N.HC_ERR_INVALID_ARG
+    for r in (-1, 9):   # the sliding-box proxy takes radius 0..8
+        p2 = N.hc_default_classify_params()
+        p2.spatial_proxy, p2.radius = 1, r
+        assert L.hc_classify(*args(p2, FAKE, need)) == N.HC_ERR_INVALID_ARG
     p3 = N.hc_default_classify_params()
     p3.rule = 3
     assert L.hc_classify(*args(p3, FAKE, need)) == N.HC_ERR_INVALID_ARG

@@ -63,7 +63,7 @@ def test_global_key_splits_merge():
 def test_sink_dummy_key_splits_merge():
     """Sink and Dummy heads alone cannot fill the GPU: the cache splits their
     key sets too and the kernel merges the partials per category."""
-    wl = W.Workload("sdsplit", 13, 4, 128, 16, 16, 4, 8, "bf16", "uniform")
+    wl = W.Workload("sdsplit", 17, 4, 128, 16, 16, 4, 8, "bf16", "uniform")
     labels = [0, 1, 1, 0]
     say("case sink/dummy split merge")
     data, cache, out = run_window(wl, labels, seed=8)

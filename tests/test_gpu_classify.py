@@ -30,7 +30,8 @@ def run_classify(wl, data, params=None):
 def oracle_head(wl, data, h, params=O.ClassifyParams()):
     fq, fk, fv = (W.as_float(data[n], wl)[h] for n in ("q", "k", "v"))
     g = geometry_of(wl)
-    outs = [O.attend_head(fq, fk, fv, p, g) for p in (O.GLOBAL, O.SINK, O.DUMMY, O.SPATIAL)]
+    sp = O.SPATIAL if params.spatial_proxy == 0 else O.SLIDING
+    outs = [O.attend_head(fq, fk, fv, p, g, radius=params.radius) for p in (O.GLOBAL, O.SINK, O.DUMMY, sp)]
     diag, cos, mse = O.head_scores(*outs, params)
     return outs, diag, cos, mse, O.decide_label(diag, params), O.decision_margin(diag, params)
 
@@ -55,6 +56,34 @@ def test_classifier_small_full_compare(name, tol, dtol):
             assert labels[h] == o_lab, (h, labels[h], o_lab, o_diag)
     if name == "planted-small":
         np.testing.assert_array_equal(labels, data["labels"])
+
+
+@pytest.mark.parametrize("name,radius", [("tiny", 2), ("planted-small", 2), ("planted-small", 1), ("d64", 3)])
+def test_classifier_sliding_box_proxy(name, radius):
+    """spatial_proxy 1: the Spatial proxy is the (2r+1)^2 box around each
+    query in every window frame.  Grids are not multiples of the query
+    patches, so border patches are ragged and boxes are cut at the edges."""
+    if name == "tiny":
+        wl = W.WORKLOADS["tiny"]
+        data, tol, dtol = W.window(wl, seed=0), FP32_TOL, 1e-5
+    elif name == "planted-small":
+        wl = W.small(W.WORKLOADS["classifier720p"], grid_h=20, grid_w=30, heads=12, window_frames=9)
+        data, tol, dtol = W.window(wl, seed=2), BF16_TOL, 1e-2
+    else:
+        wl = W.Workload("box64", 18, 3, 64, 11, 37, 2, 6, "bf16", "uniform")
+        data, tol, dtol = W.window(wl, seed=9), BF16_TOL, 1e-2
+    say("case classify sliding box", name, "r", radius)
+    p = hk.hc_default_classify_params()
+    p.spatial_proxy, p.radius = 1, radius
+    op = O.ClassifyParams(spatial_proxy=1, radius=radius)
+    labels, diag, outs, cos = run_classify(wl, data, p)
+    for h in range(wl.heads):
+        o_outs, o_diag, o_cos, _, o_lab, margin = oracle_head(wl, data, h, op)
+        check_close(outs[3, h].cpu().numpy()[None], o_outs[3][None], tol, f"{name} head {h} box output")
+        np.testing.assert_allclose(cos[h, :3].cpu().numpy(), o_cos, atol=dtol)
+        np.testing.assert_allclose(diag[h], o_diag, atol=dtol)
+        if margin > 10 * dtol:
+            assert labels[h] == o_lab, (h, labels[h], o_lab, o_diag)
 
 
 def test_classifier_rule_variants_and_percentile():
