@@ -15,6 +15,10 @@ Workloads (all Q/K/V entries i.i.d. N(0,1) unless stated):
   1080p           bf16, 40 heads, d=128, grid 68x120, block 3, window 21, same mix
   classifier720p  bf16, 40 heads at the 720p shape with planted structure
                   (see `planted_window`)
+  classifier720p_graded  the same, each planted head's key offset scaled by
+                  a seeded strength u ~ U(0, 0.25): a full offset raises the
+                  target keys' logits by about 34, so heads at u ~ 0.1 sit
+                  near the cosine thresholds (threshold studies)
 
 Random streams: numpy SeedSequence([seed, workload_id, head, tensor_id]) ->
 PCG64 -> standard_normal(float32) -> bf16 by round-to-nearest-even, so any
@@ -68,10 +72,11 @@ WORKLOADS = {
     "720p": Workload("720p", 2, 12, 128, 45, 80, 3, 21, "bf16", "mix"),
     "1080p": Workload("1080p", 3, 40, 128, 68, 120, 3, 21, "bf16", "mix"),
     "classifier720p": Workload("classifier720p", 4, 40, 128, 45, 80, 3, 21, "bf16", "planted"),
+    "classifier720p_graded": Workload("classifier720p_graded", 5, 40, 128, 45, 80, 3, 21, "bf16", "graded"),
 }
 
 # tensor ids inside a (seed, workload, head) stream family
-_T_Q, _T_PLANT, _T_LABEL = 0, 1, 2
+_T_Q, _T_PLANT, _T_LABEL, _T_STRENGTH = 0, 1, 2, 3
 _T_BLOCK_K, _T_BLOCK_V = 16, 17        # + 2 * block index
 
 
@@ -211,7 +216,7 @@ def window(wl: Workload, seed: int = 0, heads=None, threads: int = 8):
     Returns dict with q [h, Nq, d], k, v [h, Nk, d] in storage form (float32
     or bf16 bits), `labels` int8 [H] (all heads) and `heads` (the indices
     drawn).  The window is blocks 0 .. W/B-1; the queries are the last block."""
-    if wl.labels == "planted":
+    if wl.labels in ("planted", "graded"):
         return planted_window(wl, seed, heads, threads)
     heads = list(range(wl.heads)) if heads is None else list(heads)
     q, k, v = _fill_window(wl, seed, heads, threads)
@@ -261,7 +266,15 @@ def _cell_index(wl, n_frames):
     return (y // wl.cell_h) * ncx + x // wl.cell_w
 
 
-def _plant_head(wl, seed, h, kind, q, k):
+def plant_strength(wl: Workload, seed: int = 0):
+    """Per-head multiplier of the planted key offset: 1 for the planted
+    workload, u ~ U(0, 0.25) per head for the graded one."""
+    if wl.labels != "graded":
+        return np.ones(wl.heads, dtype=np.float32)
+    return np.array([0.25 * _rng(seed, wl, h, _T_STRENGTH).random() for h in range(wl.heads)], dtype=np.float32)
+
+
+def _plant_head(wl, seed, h, kind, q, k, strength=1.0):
     """Add the planted structure to one head's float32 q [Nq,d], k [Nk,d] in place."""
     if kind == NONE_KIND:
         return
@@ -272,7 +285,7 @@ def _plant_head(wl, seed, h, kind, q, k):
         q += mu
         qm = as_float(_encode(q, wl), wl).mean(axis=0, dtype=np.float64).astype(np.float32)
         rows = slice(0, B * T) if kind == SINK else slice(wl.Nk - B * T, wl.Nk)
-        k[rows] += 3.0 * qm
+        k[rows] += np.float32(3.0 * strength) * qm
         return
     # Spatial: one offset per cell
     qcell = _cell_index(wl, B)
@@ -283,15 +296,17 @@ def _plant_head(wl, seed, h, kind, q, k):
     qs = as_float(_encode(q, wl), wl)
     for c in range(ncell):
         qm = qs[qcell == c].mean(axis=0, dtype=np.float64).astype(np.float32)
-        k[kcell == c] += 3.0 * qm
+        k[kcell == c] += np.float32(3.0 * strength) * qm
 
 
 def planted_window(wl: Workload, seed: int = 0, heads=None, threads: int = 8):
     heads = list(range(wl.heads)) if heads is None else list(heads)
     kinds = planted_kinds(wl, seed)
+    strength = plant_strength(wl, seed)
     q, k, v = _fill_window(wl, seed, heads, threads,
-                           plant=lambda h, fq, fk: _plant_head(wl, seed, h, int(kinds[h]), fq, fk))
-    return {"q": q, "k": k, "v": v, "heads": heads, "labels": kinds}
+                           plant=lambda h, fq, fk: _plant_head(wl, seed, h, int(kinds[h]), fq, fk,
+                                                               float(strength[h])))
+    return {"q": q, "k": k, "v": v, "heads": heads, "labels": kinds, "strength": strength}
 
 
 def small(wl: Workload, grid_h=None, grid_w=None, heads=None, window_frames=None, name=None):
