@@ -387,9 +387,11 @@ void attn_bf16_kernel(const AttnPlan P) {
   // Software pipeline over key tiles, 4 LDS buffers (tile j lives in buffer
   // j mod 4).  Step `it` holds V of tile it and K of tile it+1 while tile it+2
   // is landing and tile it+3 is being loaded; it computes S of tile it+1 in
-  // the same instruction stream as the softmax of tile it, so the matrix core
-  // works while the vector unit exponentiates.  Tiles past the end are
-  // clamped copies of the last one (finite, unused).
+  // the same instruction stream as the softmax of tile it, so neither waits on
+  // the other's results (on this chip vector work does not run under the
+  // matrix core, so the gain is the removed dependency stall, not
+  // concurrency).  Tiles past the end are clamped copies of the last one
+  // (finite, unused).
   load_tile(0, smem0);
   load_tile(tile_base(min(1, ntiles - 1)), smem1);
   load_tile(tile_base(min(2, ntiles - 1)), smem2);
@@ -400,8 +402,10 @@ void attn_bf16_kernel(const AttnPlan P) {
   const bf16x8 ones8 = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f,
                         (__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
   auto step = [&](const int it, const uint8_t* vbuf, const uint8_t* kbuf, uint8_t* lbuf) {
-    load_tile(tile_base(min(it + 3, ntiles - 1)), lbuf);
-
+    // Tile it+3 goes into the buffer tile it-1 left (all its reads were before
+    // the last barrier).  Active waves issue its loads between the PV MFMAs
+    // (below), where the issue costs least; idle waves issue them at once.
+    const int lb3 = tile_base(min(it + 3, ntiles - 1));
     if (wave_active) {
       // Keys tile `it` must not count: rows repeated from the previous tile
       // (shifted last tile, lb + j < it*KTILE) or past a short key set.
@@ -494,6 +498,7 @@ void attn_bf16_kernel(const AttnPlan P) {
       // feed different accumulators.
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
+        if (kk == 1) load_tile(lb3, lbuf);
 #pragma unroll
         for (int t = 0; t < D / 32; ++t) {
           typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -509,6 +514,8 @@ void attn_bf16_kernel(const AttnPlan P) {
       }
 #pragma unroll
       for (int b = 0; b < QB; ++b) sc[b][0] = sn[b][0], sc[b][1] = sn[b][1];
+    } else {
+      load_tile(lb3, lbuf);
     }
     tile_barrier();   // tile it+2 is in LDS (all waves)
   };
