@@ -9,7 +9,8 @@
 // A work group is NW waves; each wave owns QB blocks of 32 queries, so a work
 // group owns 32*QB*NW queries and streams the key set in 64-key tiles through
 // a ring of four LDS buffers with online softmax, software-pipelined so that
-// the scores of the next tile are computed alongside this tile's softmax.  Per wave and key tile:
+// the scores of the next tile are computed alongside this tile's softmax.
+// Per wave and key tile:
 //   S^T (64 keys x 32 queries) = K_tile . Q^T      per query block: 2 x D/16 v_mfma_f32_32x32x16_bf16
 //   O^T (D x 32)             += V_tile^T . P^T     per query block: D/32 x 4 MFMAs
 // Computing S transposed puts one query per lane (32 scores per lane, the
@@ -95,33 +96,6 @@ template <int D>
 __device__ __forceinline__ int swz_k(int r) { return r & (Tile<D>::CPR - 1); }
 template <int D>
 __device__ __forceinline__ int swz_v(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
-
-struct CellInfo {
-  int base;    // y0*grid_w + x0
-  int size;    // |c|
-  int width;   // cell width (x extent)
-  int off;     // sum of |c'| over cells c' < c
-};
-
-__device__ __forceinline__ CellInfo cell_info(const AttnPlan& P, int c) {
-  const int cy = c / P.cell_cols, cx = c - cy * P.cell_cols;
-  const int y0 = cy * P.cell_h, x0 = cx * P.cell_w;
-  const int h = min(P.cell_h, P.grid_h - y0), w = min(P.cell_w, P.grid_w - x0);
-  CellInfo ci;
-  ci.base = y0 * P.grid_w + x0;
-  ci.size = h * w;
-  ci.width = w;
-  ci.off = cy * P.cell_h * P.grid_w + cx * h * P.cell_w;
-  return ci;
-}
-
-// Token row of the i-th element of a cell, enumerated frame by frame.
-__device__ __forceinline__ int cell_token(const AttnPlan& P, const CellInfo& c, int i) {
-  const int f = i / c.size;
-  const int r = i - f * c.size;
-  const int ry = r / c.width;
-  return f * P.T + c.base + ry * P.grid_w + (r - ry * c.width);
-}
 
 // Initial running max: finite, so that a tile whose keys are all masked for a
 // query (box proxy) gives exp2(-inf) = 0 instead of exp2(-inf + inf) = NaN.

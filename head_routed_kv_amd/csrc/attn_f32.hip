@@ -14,24 +14,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int NT = 256;
 constexpr int FKT = 32;   // keys per LDS tile
 
-struct CellInfo {
-  int base, size, width, off;
-};
-
-__device__ __forceinline__ CellInfo cell_info(const AttnPlan& P, int c) {
-  const int cy = c / P.cell_cols, cx = c - cy * P.cell_cols;
-  const int y0 = cy * P.cell_h, x0 = cx * P.cell_w;
-  const int h = min(P.cell_h, P.grid_h - y0), w = min(P.cell_w, P.grid_w - x0);
-  return CellInfo{y0 * P.grid_w + x0, h * w, w, cy * P.cell_h * P.grid_w + cx * h * P.cell_w};
-}
-
-__device__ __forceinline__ int cell_token(const AttnPlan& P, const CellInfo& c, int i) {
-  const int f = i / c.size;
-  const int r = i - f * c.size;
-  const int ry = r / c.width;
-  return f * P.T + c.base + ry * P.grid_w + (r - ry * c.width);
-}
-
 template <int D>
 __global__ __launch_bounds__(NT) void attn_f32_kernel(const AttnPlan P) {
   constexpr int H2 = D / 2;

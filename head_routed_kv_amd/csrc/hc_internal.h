@@ -81,6 +81,35 @@ struct AttnPlan {
   uint8_t head_of[4][HC_MAX_HEADS];  // category slot -> q/o head index
 };
 
+struct CellInfo {
+  int base;    // y0*grid_w + x0
+  int size;    // |c|
+  int width;   // cell width (x extent)
+  int off;     // sum of |c'| over cells c' < c
+};
+
+// Latent cell c (row-major over the cell grid, cells anchored at (0,0) and cut
+// at the frame edge) and where its rows sit in the cell-major Spatial buffer.
+__device__ __forceinline__ CellInfo cell_info(const AttnPlan& P, int c) {
+  const int cy = c / P.cell_cols, cx = c - cy * P.cell_cols;
+  const int y0 = cy * P.cell_h, x0 = cx * P.cell_w;
+  const int h = min(P.cell_h, P.grid_h - y0), w = min(P.cell_w, P.grid_w - x0);
+  CellInfo ci;
+  ci.base = y0 * P.grid_w + x0;
+  ci.size = h * w;
+  ci.width = w;
+  ci.off = cy * P.cell_h * P.grid_w + cx * h * P.cell_w;
+  return ci;
+}
+
+// Token row of the i-th element of a cell, enumerated frame by frame.
+__device__ __forceinline__ int cell_token(const AttnPlan& P, const CellInfo& c, int i) {
+  const int f = i / c.size;
+  const int r = i - f * c.size;
+  const int ry = r / c.width;
+  return f * P.T + c.base + ry * P.grid_w + (r - ry * c.width);
+}
+
 // Patch of a KIND_BOX_GATHER unit: block frame, first query row and column.
 struct BoxInfo {
   int fb, py0, px0;

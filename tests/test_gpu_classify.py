@@ -1,5 +1,6 @@
 """GPU parity of the one-shot classifier (hc_classify) against the CPU oracle:
 the four outputs, per-query cosines, per-head diagnostics and labels."""
+import functools
 import json
 import os
 
@@ -103,13 +104,18 @@ def test_classifier_rule_variants_and_percentile():
             assert labels[h] == o_lab
 
 
+@functools.lru_cache(maxsize=1)
+def planted_720p():
+    return W.window(W.WORKLOADS["classifier720p"], seed=0)
+
+
 def test_classifier_720p_planted_golden():
     """40 planted heads at the 720p shape: labels bit-exact against the
     oracle's stored result, diagnostics within tolerance."""
     path = os.path.join(GOLDEN, "classifier720p_seed0.json")
     gold = json.load(open(path))
     wl = W.WORKLOADS["classifier720p"]
-    data = W.window(wl, seed=0)
+    data = planted_720p()
     say("case classify 720p planted")
     labels, diag, outs, cos = run_classify(wl, data)
     assert min(gold["margin"]) > 1e-2
