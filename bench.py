@@ -249,6 +249,12 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the 1080p and per-pathway figures")
+    ap.add_argument("--theta", type=float, default=0.95, help="classifier cosine threshold (all three proxies)")
+    ap.add_argument("--theta-sc", type=float, default=0.755, help="classifier Spatial score threshold")
+    ap.add_argument("--gamma", type=float, default=5.0, help="classifier MSE weight")
+    ap.add_argument("--percentile", type=float, default=5.0, help="classifier Spatial cosine percentile")
+    ap.add_argument("--rule", type=int, default=0, choices=(0, 1), help="classifier rule")
+    ap.add_argument("--radius", type=int, default=2, help="sliding-box proxy radius")
     ap.add_argument("--calibrate", action="store_true",
                     help="also run a plain 1 GiB device copy (known bytes) to scale HBM counters")
     a = ap.parse_args()
@@ -347,10 +353,13 @@ def main():
         wl3 = W.WORKLOADS["classifier720p"]
         q3, k3, v3 = gen_inputs(wl3, a.seed + 2, dev)
         cfg3 = hk.make_config(wl3.heads, wl3.head_dim, wl3.grid_h, wl3.grid_w, wl3.block_frames, wl3.window_frames)
+        pg = hk.hc_default_classify_params()
+        pg.theta_sink = pg.theta_dummy = pg.theta_spatial = a.theta
+        pg.theta_score, pg.gamma, pg.percentile, pg.rule = a.theta_sc, a.gamma, a.percentile, a.rule
         ws = None
         for _ in range(2):
-            _, _, ws = hk.classify(cfg3, q3, k3, v3, workspace=ws)
-        cls_ms = time_events(lambda: hk.classify(cfg3, q3, k3, v3, workspace=ws), 3)
+            _, _, ws = hk.classify(cfg3, q3, k3, v3, pg, workspace=ws)
+        cls_ms = time_events(lambda: hk.classify(cfg3, q3, k3, v3, pg, workspace=ws), 3)
         BT = wl3.Nq
         pairs = wl3.Nq * wl3.Nk + 2 * wl3.Nq * BT + \
             wl3.block_frames * wl3.window_frames * sum(c * c for c in cell_sizes(wl3.grid_h, wl3.grid_w))
@@ -359,12 +368,14 @@ def main():
                                    "mfma_frac": round(f3 / (cls_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
         # the same with the pages' sliding 5x5 box as the Spatial proxy
         pb = hk.hc_default_classify_params()
-        pb.spatial_proxy, pb.radius = 1, 2
+        pb.theta_sink = pb.theta_dummy = pb.theta_spatial = a.theta
+        pb.theta_score, pb.gamma, pb.percentile, pb.rule = a.theta_sc, a.gamma, a.percentile, a.rule
+        pb.spatial_proxy, pb.radius = 1, a.radius
         for _ in range(2):
             hk.classify(cfg3, q3, k3, v3, pb, workspace=ws)
         box_ms = time_events(lambda: hk.classify(cfg3, q3, k3, v3, pb, workspace=ws), 3)
         pairs_b = wl3.Nq * wl3.Nk + 2 * wl3.Nq * BT + \
-            wl3.block_frames * wl3.window_frames * box_span(wl3.grid_h, 2) * box_span(wl3.grid_w, 2)
+            wl3.block_frames * wl3.window_frames * box_span(wl3.grid_h, a.radius) * box_span(wl3.grid_w, a.radius)
         fb = wl3.heads * 4 * wl3.head_dim * pairs_b
         extra["classifier720p_box"] = {"heads": wl3.heads, "ms": round(box_ms, 3),
                                        "tflops": round(fb / (box_ms / 1e3) / 1e12, 1),

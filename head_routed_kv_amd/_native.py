@@ -8,7 +8,8 @@ import ctypes as C
 import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libheadcast.so")
+# HEADCAST_LIB selects another build of the same library (e.g. the host-ASan one).
+LIB_PATH = os.environ.get("HEADCAST_LIB") or os.path.join(_PKG, "libheadcast.so")
 
 HC_MAX_HEADS = 128
 HC_OK, HC_ERR_INVALID_ARG, HC_ERR_SHAPE, HC_ERR_DTYPE, HC_ERR_ALIGN = 0, -1, -2, -3, -4

@@ -115,6 +115,21 @@ def test_misuse_is_rejected_before_launch():
     assert L.hc_cache_destroy(None) == N.HC_ERR_INVALID_ARG
 
 
+def test_launch_failure_is_reported_as_hip_error():
+    """A valid call whose kernel launch fails returns HC_ERR_HIP and names the
+    step.  Forced here by the absence of a GPU, so it runs only on a host
+    without one (elsewhere the call would really launch on a fake pointer)."""
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is visible: this call would launch")
+    c = cfg()
+    h = N.hc_cache_create(c, [0, 1, 2, 3], FAKE, N.hc_cache_bytes(c, [0, 1, 2, 3]))
+    kv = N.hc_tensor(FAKE, 96 * 128, 128)
+    assert N.lib().hc_cache_append(h, kv, kv, N.HC_PUSH_BLOCK, None) == N.HC_ERR_HIP
+    assert b"append" in N.lib().hc_last_error_message()
+    N.hc_cache_destroy(h)
+
+
 def test_classify_argument_checks():
     c = cfg()
     L = N.lib()

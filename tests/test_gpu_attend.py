@@ -181,6 +181,26 @@ def test_full_size_sampled_rows(name):
     say(name, "worst err/rms", worst, "splits", cache.layout().global_splits)
 
 
+@pytest.mark.parametrize("lab", [O.GLOBAL, O.SINK, O.DUMMY, O.SPATIAL])
+def test_720p_pathway_alone_sampled(lab):
+    """Each pathway's heads of the 720p layer alone, as the benchmark's
+    per-pathway figures run them: few heads, so ranged key sets are split
+    (Global, Sink and Dummy alike) and merged in the kernel."""
+    wl = W.WORKLOADS["720p"]
+    heads = [h for h in range(wl.heads) if int(W.make_labels(wl)[h]) == lab]
+    sub = W.small(wl, heads=len(heads))
+    say("case 720p alone, pathway", lab, "heads", len(heads))
+    data, cache, out = run_window(sub, [lab] * len(heads), seed=4)
+    lay = cache.layout()
+    if lab != O.SPATIAL:
+        assert max(lay.global_splits, lay.sink_splits, lay.dummy_splits) > 1
+    rows = sample_rows(sub, 48, seed=lab)
+    fq, fk, fv = (W.as_float(data[n], sub) for n in ("q", "k", "v"))
+    g = geometry_of(sub)
+    ref = np.stack([O.attend_head(fq[h], fk[h], fv[h], lab, g, rows=rows) for h in range(len(heads))])
+    check_close(to_float(out)[:, rows], ref, BF16_TOL, f"pathway {lab} alone")
+
+
 def test_full_attention_baseline_720p_sampled():
     """All heads Global is the full-attention baseline the speedup is taken over."""
     wl = W.WORKLOADS["720p"]
