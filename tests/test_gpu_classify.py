@@ -128,3 +128,23 @@ def test_classifier_720p_planted_golden():
         fq, fk, fv = (W.as_float(data[n], wl)[h] for n in ("q", "k", "v"))
         ref = O.attend_head(fq, fk, fv, O.GLOBAL, g, rows=rows)
         check_close(outs[0, h].cpu().numpy()[rows][None], ref[None], BF16_TOL, f"720p full output head {h}")
+
+
+def test_classifier_720p_planted_golden_box():
+    """The same 40 planted heads with the sliding 5x5 box proxy: labels
+    bit-exact against the oracle's stored result, diagnostics within
+    tolerance.  The two stored oracle results also fix the proxy-agreement
+    figure: box and grid proxies agree on the heads whose structure is not
+    tied to the grid cells."""
+    gold = json.load(open(os.path.join(GOLDEN, "classifier720p_box_seed0.json")))
+    grid = json.load(open(os.path.join(GOLDEN, "classifier720p_seed0.json")))
+    assert gold["spatial_proxy"] == 1 and gold["radius"] == 2 and min(gold["margin"]) > 1e-2
+    wl = W.WORKLOADS["classifier720p"]
+    say("case classify 720p planted, sliding box")
+    p = hk.hc_default_classify_params()
+    p.spatial_proxy, p.radius = 1, 2
+    labels, diag, _, _ = run_classify(wl, planted_720p(), p)
+    np.testing.assert_array_equal(labels, np.array(gold["labels"], dtype=np.int8))
+    np.testing.assert_allclose(diag, np.array(gold["diag"]), atol=1e-2)
+    box, cell = np.array(gold["labels"]), np.array(grid["labels"])
+    say("box/grid label agreement", int((box == cell).sum()), "of", wl.heads)
