@@ -142,9 +142,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2 / QB, 2 / 
 void attn_bf16_kernel(const AttnPlan P) {
   using TL = Tile<D>;
   constexpr int QT = 32 * QB * NW;   // queries per work group
-  // Two distinct LDS objects (not one indexed array), so the compiler can see
-  // that the next tile's LDS-DMA writes never alias this tile's reads and does
-  // not make the reads wait for the loads.
+  // The four ring buffers (K tile then V tile each); tile j lives in buffer
+  // j mod 4.  Separate objects rather than one indexed array, so every LDS
+  // address in the unrolled loop is a constant plus a per-lane offset.
   __shared__ __attribute__((aligned(16))) uint8_t smem0[TL::BUF];
   __shared__ __attribute__((aligned(16))) uint8_t smem1[TL::BUF];
   __shared__ __attribute__((aligned(16))) uint8_t smem2[TL::BUF];
@@ -513,8 +513,9 @@ void attn_bf16_kernel(const AttnPlan P) {
   if (splits > 1) {
     // Write this split's unnormalised partial, count it, and let the last split
     // to arrive merge.  The partials and the counter are accessed only with
-    // device-coherent (sc1) operations, which reach the memory side past the
-    // per-XCD L2s, so no fence has to write back or invalidate a whole L2.
+    // device-scope atomic operations (relaxed; sc1 on this chip), which are
+    // coherent across the XCDs' separate L2 caches by themselves, so no fence
+    // has to write back or invalidate a whole L2 (an agent-scope fence does).
     // Partial layout per (id, split): O as [D/2][QT] float2 (consecutive
     // queries adjacent), then (m, l) as [QT] float2 after all O planes.
     const int id = slot * P.q_tiles + tile;
