@@ -188,22 +188,36 @@ def box_span(n, r):
     return sum(min(p + r, n - 1) - max(p - r, 0) + 1 for p in range(n))
 
 
+def source_fingerprint(paths):
+    """SHA-256 of the code in `paths` with comments and whitespace removed
+    (// and /* */ in C/HIP sources, # in Python), so that a comment edit does
+    not count as a kernel change and any code edit does."""
+    import hashlib
+    import re
+    h = hashlib.sha256()
+    for src in paths:
+        text = open(os.path.join(ROOT, src), encoding="utf-8").read()
+        if src.endswith(".py"):
+            text = re.sub(r"#[^\n]*", " ", text)
+        else:
+            text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+            text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
+    return h.hexdigest()
+
+
 def counter_traffic(workload):
     """HBM bytes per launch of the attention kernel from the committed
     rocprofv3 FETCH_SIZE / WRITE_SIZE record, scaled by its copy calibration.
-    None unless the record's source hash matches the sources built now (the
-    counters describe a kernel that no longer exists otherwise) and it was
-    taken on this workload."""
-    import hashlib
+    None unless the record's source fingerprint matches the sources built now
+    (the counters describe a kernel that no longer exists otherwise) and it
+    was taken on this workload."""
     path = os.path.join(ROOT, "profiles", f"traffic_attn_bf16_{workload}_routed.json")
     if not os.path.exists(path):
         return None
     try:
         rec = json.load(open(path))
-        h = hashlib.sha256()
-        for src in rec["sources"]:
-            h.update(open(os.path.join(ROOT, src), "rb").read())
-        if h.hexdigest() != rec["sources_sha256"]:
+        if source_fingerprint(rec["sources"]) != rec["sources_fingerprint"]:
             return None
         return int(rec["traffic_bytes"])
     except (OSError, ValueError, KeyError, TypeError):
