@@ -214,20 +214,26 @@ void attn_bf16_kernel(const AttnPlan P) {
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
+  // Units with at most 64 queries (the ragged last q tile of a head, the short
+  // remainder sub-tile of a cell) would leave six of eight waves idle.  They
+  // run their own schedule instead: waves 0-3 take query block (w & 1) and
+  // every other key tile (half w >> 1), and the halves merge through LDS.
+  const bool small = QB == 1 && !is_box && qn <= 64;
+
   // ---- this lane's query rows (one per query block) -----------------------
   int qlocal[QB], qtok[QB];
   bool qvalid[QB];
   bf16x8 qb[QB][D / 16];
 #pragma unroll
   for (int b = 0; b < QB; ++b) {
-    qlocal[b] = wave * 32 * QB + 32 * b + l32;
+    qlocal[b] = small ? 32 * (wave & 1) + l32 : wave * 32 * QB + 32 * b + l32;
     qtok[b] = 0;
     if (is_box) {   // patch row wave*QB+b, column l32
       const int y = box.py0 + wave * QB + b, x = box.px0 + l32;
       qvalid[b] = l32 < P.box_cols_q && y < P.grid_h && x < P.grid_w;
       if (qvalid[b]) qtok[b] = box.fb * P.T + y * P.grid_w + x;
     } else {
-      qvalid[b] = qlocal[b] < qn;
+      qvalid[b] = qlocal[b] < qn && (!small || wave < 4);
       if (qvalid[b]) qtok[b] = ranged ? (q0 + qlocal[b]) : cell_token(P, cell, q0 + qlocal[b]);
     }
     const uint16_t* qrow = Qb + (int64_t)qtok[b] * P.q_st + 8 * hi;
@@ -238,7 +244,8 @@ void attn_bf16_kernel(const AttnPlan P) {
       qb[b][s] = __builtin_bit_cast(bf16x8, w);
     }
   }
-  const bool wave_active = is_box ? (box.py0 + wave * QB < P.grid_h) : (wave * 32 * QB < qn);
+  bool wave_active = is_box ? (box.py0 + wave * QB < P.grid_h)
+                   : small ? (wave < 4 && 32 * (wave & 1) < qn) : (wave * 32 * QB < qn);
   // Box proxy: bit rx of box_cm says whether this lane's query may see box
   // column rx (within r columns of it, and on the grid), shifted so that bit
   // 8a+e stands for column 8a+4*hi+e, the keys this lane's score registers hold.
@@ -366,6 +373,9 @@ void attn_bf16_kernel(const AttnPlan P) {
   // matrix core, so the gain is the removed dependency stall, not
   // concurrency).  Tiles past the end are clamped copies of the last one
   // (finite, unused).
+  const bf16x8 ones8 = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f,
+                        (__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
+  if (!small) {
   load_tile(0, smem0);
   load_tile(tile_base(min(1, ntiles - 1)), smem1);
   load_tile(tile_base(min(2, ntiles - 1)), smem2);
@@ -373,8 +383,6 @@ void attn_bf16_kernel(const AttnPlan P) {
   f32x16 sc[QB][2];
   scores(smem0, sc);
 
-  const bf16x8 ones8 = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f,
-                        (__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
   auto step = [&](const int it, const uint8_t* vbuf, const uint8_t* kbuf, uint8_t* lbuf) {
     // Tile it+3 goes into the buffer tile it-1 left (all its reads were before
     // the last barrier).  Active waves issue its loads between the PV MFMAs
@@ -498,6 +506,144 @@ void attn_bf16_kernel(const AttnPlan P) {
     if (it + 1 < ntiles) step(it + 1, smem1, smem2, smem0);
     if (it + 2 < ntiles) step(it + 2, smem2, smem3, smem1);
     if (it + 3 < ntiles) step(it + 3, smem3, smem0, smem2);
+  }
+  } else if constexpr (QB == 1) {
+    // ---- small units: two key halves in parallel ---------------------------
+    // Pair p = tiles 2p (half 0) and 2p+1 (half 1), in buffers (0,1) for even
+    // p and (2,3) for odd p; pair p+2 is loaded as soon as pair p has been
+    // read.  Not pipelined: each wave computes the scores, softmax and PV of
+    // its tile in turn.
+    const int half = (wave >> 1) & 1;
+    const int npairs = (ntiles + 1) >> 1;
+    auto tb = [&](int t) { return tile_base(min(t, ntiles - 1)); };
+    auto wait_pair = [&]() {   // all but the newest pair's 4*LPW loads have landed
+      if constexpr (4 * TL::LPW == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      else if constexpr (4 * TL::LPW == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    };
+    auto barrier = [&]() {
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    };
+    load_tile(tb(0), smem0);
+    load_tile(tb(1), smem1);
+    load_tile(tb(2), smem2);
+    load_tile(tb(3), smem3);
+    auto pair_step = [&](const int p, uint8_t* b0, uint8_t* b1) {
+      wait_pair();
+      barrier();   // pair p is in LDS
+      const int it = 2 * p + half;
+      const uint8_t* buf = half ? b1 : b0;
+      if (wave_active && it < ntiles) {
+        f32x16 st[2];
+        {
+          f32x16 tmp[QB][2];
+          scores(buf, tmp);
+          st[0] = tmp[0][0];
+          st[1] = tmp[0][1];
+        }
+        const int lo = it * KTILE - tile_base(it);
+        const int hi_end = short_set ? kn : KTILE;
+        if (lo > 0 || hi_end < KTILE) {
+#pragma unroll
+          for (int jj = 0; jj < 16; ++jj) {
+            const int key = 8 * (jj >> 2) + 4 * hi + (jj & 3);
+            if (key < lo || key >= hi_end) st[0][jj] = -INFINITY;
+            if (key + 32 < lo || key + 32 >= hi_end) st[1][jj] = -INFINITY;
+          }
+        }
+        float mx = st[0][0];
+#pragma unroll
+        for (int jj = 1; jj < 16; ++jj) mx = fmaxf(mx, st[0][jj]);
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) mx = fmaxf(mx, st[1][jj]);
+        {
+          const Pair pr = halves(mx);
+          mx = fmaxf(pr.a, pr.b);
+        }
+        const bool grow = mx * c2 > fmaf(m_run[0], c2, kLazyLog2);
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+          const float m_new = grow ? mx : m_run[0];
+          const float alpha = __builtin_amdgcn_exp2f((m_run[0] - m_new) * c2);
+          l_run[0] *= alpha;
+#pragma unroll
+          for (int t = 0; t < D / 32; ++t) oacc[0][t] *= alpha;
+          m_run[0] = m_new;
+        }
+        const float mc = m_run[0] * c2;
+        bf16x8 pbs[4];
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) {
+          st[0][jj] = __builtin_amdgcn_exp2f(fmaf(st[0][jj], c2, -mc));
+          st[1][jj] = __builtin_amdgcn_exp2f(fmaf(st[1][jj], c2, -mc));
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          pbs[0][e] = (__bf16)st[0][e];
+          pbs[1][e] = (__bf16)st[0][8 + e];
+          pbs[2][e] = (__bf16)st[1][e];
+          pbs[3][e] = (__bf16)st[1][8 + e];
+        }
+        float psum = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+            const bf16x2 p2 = {pbs[kk][2 * e], pbs[kk][2 * e + 1]};
+            const bf16x2 o2 = {ones8[0], ones8[1]};
+            psum = __builtin_amdgcn_fdot2_f32_bf16(p2, o2, psum, false);
+          }
+        l_run[0] += psum;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+          for (int t = 0; t < D / 32; ++t) {
+            typedef short s16x4 __attribute__((ext_vector_type(4)));
+            const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (s16x4 __attribute__((address_space(3)))*)((lds_u8*)buf + TL::KB + vt_addr(t, kk, 0)));
+            const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (s16x4 __attribute__((address_space(3)))*)((lds_u8*)buf + TL::KB + vt_addr(t, kk, 1)));
+            const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+            oacc[0][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pbs[kk], oacc[0][t], 0, 0, 0);
+          }
+      }
+      barrier();   // pair p has been read by every wave
+      load_tile(tb(2 * p + 4), b0);   // pair p+2 (clamped copies past the end)
+      load_tile(tb(2 * p + 5), b1);
+    };
+    for (int p = 0; p < npairs; p += 2) {
+      pair_step(p, smem0, smem1);
+      if (p + 1 < npairs) pair_step(p + 1, smem2, smem3);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    barrier();   // every LDS read and load done: the buffers are free
+    // waves 2, 3 hand their half (O, m, l) to waves 0, 1 of the same block
+    constexpr int NV = 16 * (D / 32);
+    float* xfer = (float*)((wave & 1) ? smem1 : smem0);
+    if (wave == 2 || wave == 3) {
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) xfer[(16 * t + i) * 64 + lane] = oacc[0][t][i];
+      xfer[NV * 64 + lane] = m_run[0];
+      xfer[(NV + 1) * 64 + lane] = l_run[0];
+    }
+    __syncthreads();
+    if (wave < 2) {
+      const float mb = xfer[NV * 64 + lane], lb = xfer[(NV + 1) * 64 + lane];
+      const float M = fmaxf(m_run[0], mb);
+      const float aa = __builtin_amdgcn_exp2f((m_run[0] - M) * c2);
+      const float ab = __builtin_amdgcn_exp2f((mb - M) * c2);
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[0][t][i] = oacc[0][t][i] * aa + xfer[(16 * t + i) * 64 + lane] * ab;
+      l_run[0] = l_run[0] * aa + lb * ab;
+      m_run[0] = M;
+    }
+    wave_active = wave_active && wave < 2;
+    qvalid[0] = qvalid[0] && wave < 2;
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no LDS load may outlive the work group
 

@@ -81,10 +81,13 @@ def check_close(got, ref, tol, what=""):
 
 def sample_rows(wl, n=48, seed=0):
     """Query rows to check at full size: both ends (ragged last q tile), the
-    frame seams, border-cell rows and a seeded random spread."""
+    frame seams, border-cell rows, the last query of the first cell (in the
+    cell's short remainder sub-tile when a cell holds more queries than one
+    work group) and a seeded random spread."""
     rng = np.random.default_rng(seed)
     T, Nq, gw = wl.T, wl.Nq, wl.grid_w
-    fixed = [0, 1, 127, 128, Nq - 1, Nq - 2, T - 1, T, gw - 1, T - gw, Nq - gw]
+    last_of_cell0 = (wl.block_frames - 1) * T + (min(wl.cell_h, wl.grid_h) - 1) * gw + min(wl.cell_w, gw) - 1
+    fixed = [0, 1, 127, 128, Nq - 1, Nq - 2, T - 1, T, gw - 1, T - gw, Nq - gw, last_of_cell0]
     rows = set(r for r in fixed if 0 <= r < Nq)
     rows.update(rng.integers(0, Nq, n - len(rows)).tolist())
     return np.array(sorted(rows))
