@@ -348,6 +348,22 @@ void attn_bf16_kernel(const AttnPlan P) {
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
+  // Scores of key slots j < lo or j >= hi_end become -inf.  Score jj of half c
+  // is key slot 32c + 8(jj/4) + 4hi + jj%4; compared against lane-relative
+  // bounds, every slot offset is a constant.  The bounds are opaque to the
+  // compiler, which would otherwise hoist the 32 lane masks of the loop-invariant
+  // end bound out of the loop into (spilled) scalar registers.
+  auto mask_keys = [&](f32x16 (&s)[2], const int lo, const int hi_end) {
+    int lo_l = lo - 4 * hi, he_l = hi_end - 4 * hi;
+    asm volatile("" : "+v"(lo_l), "+v"(he_l));   // keep the 32 compares in this branch
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) {
+        const int kc = 32 * c + 8 * (jj >> 2) + (jj & 3);
+        if (kc < lo_l || kc >= he_l) s[c][jj] = -INFINITY;
+      }
+  };
   // S^T of one tile: sc[b][blk] (keys 32*blk.. x 32 queries of block b).
   auto scores = [&](const uint8_t* Ks, f32x16 (&out)[QB][2]) {
 #pragma unroll
@@ -395,18 +411,13 @@ void attn_bf16_kernel(const AttnPlan P) {
       const int hi_end = short_set ? kn : KTILE;     // slots j >= hi_end are empty
       if (lo > 0 || hi_end < KTILE) {
 #pragma unroll
-        for (int jj = 0; jj < 16; ++jj) {
-          const int key = 8 * (jj >> 2) + 4 * hi + (jj & 3);
-#pragma unroll
-          for (int b = 0; b < QB; ++b) {
-            if (key < lo || key >= hi_end) sc[b][0][jj] = -INFINITY;
-            if (key + 32 < lo || key + 32 >= hi_end) sc[b][1][jj] = -INFINITY;
-          }
-        }
+        for (int b = 0; b < QB; ++b) mask_keys(sc[b], lo, hi_end);
       }
       if constexpr (GATHER) {
         if (is_box) {   // box proxy: only keys within r rows and r columns count
           const int rows = P.box_rows + 2 * P.box_r;
+          uint32_t cm = box_cm;
+          asm volatile("" : "+v"(cm));   // the 16 bit tests stay in this branch
 #pragma unroll
           for (int c = 0; c < 2; ++c) {
             const int ky = box.py0 - P.box_r + (2 * it + c) % rows;   // uniform
@@ -416,7 +427,7 @@ void attn_bf16_kernel(const AttnPlan P) {
               const bool row_ok = ky >= 0 && ky < P.grid_h && abs(ky - qy) <= P.box_r;
 #pragma unroll
               for (int jj = 0; jj < 16; ++jj)
-                if (!row_ok || !((box_cm >> (8 * (jj >> 2) + (jj & 3))) & 1u)) sc[b][c][jj] = -INFINITY;
+                if (!row_ok || !((cm >> (8 * (jj >> 2) + (jj & 3))) & 1u)) sc[b][c][jj] = -INFINITY;
             }
           }
         }
@@ -544,14 +555,7 @@ void attn_bf16_kernel(const AttnPlan P) {
         }
         const int lo = it * KTILE - tile_base(it);
         const int hi_end = short_set ? kn : KTILE;
-        if (lo > 0 || hi_end < KTILE) {
-#pragma unroll
-          for (int jj = 0; jj < 16; ++jj) {
-            const int key = 8 * (jj >> 2) + 4 * hi + (jj & 3);
-            if (key < lo || key >= hi_end) st[0][jj] = -INFINITY;
-            if (key + 32 < lo || key + 32 >= hi_end) st[1][jj] = -INFINITY;
-          }
-        }
+        if (lo > 0 || hi_end < KTILE) mask_keys(st, lo, hi_end);
         float mx = st[0][0];
 #pragma unroll
         for (int jj = 1; jj < 16; ++jj) mx = fmaxf(mx, st[0][jj]);
