@@ -398,6 +398,21 @@ void attn_bf16_kernel(const AttnPlan P) {
   tile_barrier();   // tiles 0 and 1 are in LDS
   f32x16 sc[QB][2];
   scores(smem0, sc);
+  // Row max of the tile in sc over both lanes of each query, computed one step
+  // ahead (after the PV products, where it fills the vector unit) and redone
+  // on the tiles that mask keys.
+  auto row_max = [&](const f32x16 (&s)[2]) {
+    float mx = s[0][0];
+#pragma unroll
+    for (int jj = 1; jj < 16; ++jj) mx = fmaxf(mx, s[0][jj]);
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) mx = fmaxf(mx, s[1][jj]);
+    const Pair pr = halves(mx);
+    return fmaxf(pr.a, pr.b);
+  };
+  float tmax[QB];
+#pragma unroll
+  for (int b = 0; b < QB; ++b) tmax[b] = row_max(sc[b]);
 
   auto step = [&](const int it, const uint8_t* vbuf, const uint8_t* kbuf, uint8_t* lbuf) {
     // Tile it+3 goes into the buffer tile it-1 left (all its reads were before
@@ -411,7 +426,10 @@ void attn_bf16_kernel(const AttnPlan P) {
       const int hi_end = short_set ? kn : KTILE;     // slots j >= hi_end are empty
       if (lo > 0 || hi_end < KTILE) {
 #pragma unroll
-        for (int b = 0; b < QB; ++b) mask_keys(sc[b], lo, hi_end);
+        for (int b = 0; b < QB; ++b) {
+          mask_keys(sc[b], lo, hi_end);
+          tmax[b] = row_max(sc[b]);
+        }
       }
       if constexpr (GATHER) {
         if (is_box) {   // box proxy: only keys within r rows and r columns count
@@ -430,20 +448,14 @@ void attn_bf16_kernel(const AttnPlan P) {
                 if (!row_ok || !((cm >> (8 * (jj >> 2) + (jj & 3))) & 1u)) sc[b][c][jj] = -INFINITY;
             }
           }
+#pragma unroll
+          for (int b = 0; b < QB; ++b) tmax[b] = row_max(sc[b]);
         }
       }
       float mc[QB];
 #pragma unroll
       for (int b = 0; b < QB; ++b) {
-        float mx = sc[b][0][0];
-#pragma unroll
-        for (int jj = 1; jj < 16; ++jj) mx = fmaxf(mx, sc[b][0][jj]);
-#pragma unroll
-        for (int jj = 0; jj < 16; ++jj) mx = fmaxf(mx, sc[b][1][jj]);
-        {
-          const Pair pr = halves(mx);
-          mx = fmaxf(pr.a, pr.b);
-        }
+        const float mx = tmax[b];
         const bool grow = mx * c2 > fmaf(m_run[b], c2, kLazyLog2);
         if (__builtin_amdgcn_ballot_w64(grow) != 0) {   // wave-uniform
           const float m_new = grow ? mx : m_run[b];
@@ -506,7 +518,10 @@ void attn_bf16_kernel(const AttnPlan P) {
         }
       }
 #pragma unroll
-      for (int b = 0; b < QB; ++b) sc[b][0] = sn[b][0], sc[b][1] = sn[b][1];
+      for (int b = 0; b < QB; ++b) {
+        tmax[b] = row_max(sn[b]);
+        sc[b][0] = sn[b][0], sc[b][1] = sn[b][1];
+      }
     } else {
       load_tile(lb3, lbuf);
     }
