@@ -18,6 +18,7 @@ import argparse
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -88,10 +89,10 @@ class Layer:
         self.attend()
 
 
-def time_events(fn, iters, flush=None):
-    """Average ms of fn() between HIP events on the current stream."""
+def time_samples(fn, iters, flush=None):
+    """ms of each of `iters` calls of fn(), between HIP events on the current stream."""
     import torch
-    total = 0.0
+    out = []
     for _ in range(iters):
         if flush is not None:
             flush()
@@ -101,8 +102,55 @@ def time_events(fn, iters, flush=None):
         fn()
         b.record()
         b.synchronize()
-        total += a.elapsed_time(b)
-    return total / iters
+        out.append(a.elapsed_time(b))
+    return out
+
+
+def time_events(fn, iters, flush=None):
+    """Average ms of fn() between HIP events on the current stream."""
+    return statistics.fmean(time_samples(fn, iters, flush))
+
+
+def summary(ms):
+    return {"mean": round(statistics.fmean(ms), 4), "median": round(statistics.median(ms), 4),
+            "min": round(min(ms), 4), "n": len(ms)}
+
+
+def device_info(index=0):
+    """Name, compute units and peak shader clock of the GPU (hipDeviceGetAttribute for the clock)."""
+    import ctypes
+    import torch
+    p = torch.cuda.get_device_properties(index)
+    info = {"name": p.name, "arch": p.gcnArchName.split(":")[0], "compute_units": p.multi_processor_count}
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        khz = ctypes.c_int(0)
+        if hip.hipDeviceGetAttribute(ctypes.byref(khz), 5, index) == 0:   # hipDeviceAttributeClockRate
+            info["peak_sclk_mhz"] = khz.value // 1000
+    except OSError:
+        pass
+    return info
+
+
+def ceilings(device):
+    """Achievable ceilings on this GPU, as context: a large bf16 GEMM (torch.matmul) and a device copy."""
+    import torch
+    n = 8192
+    a = torch.randn(n, n, device=device, dtype=torch.float32).to(torch.bfloat16)
+    b = torch.randn(n, n, device=device, dtype=torch.float32).to(torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, b)
+    mm = statistics.median(time_samples(lambda: torch.matmul(a, b), 10))
+    del a, b
+    src = torch.ones(1 << 28, dtype=torch.float32, device=device)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    cp = statistics.median(time_samples(lambda: dst.copy_(src), 10))
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"matmul_bf16_8192": {"ms": round(mm, 4), "tflops": round(2 * n ** 3 / (mm / 1e3) / 1e12, 1)},
+            "copy_1gib": {"ms": round(cp, 4), "gbs": round(2 * (1 << 30) / (cp / 1e3) / 1e9, 1)}}
 
 
 def make_flush(device):
@@ -309,7 +357,8 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / a.steps
-    attend_ms = sum(s.elapsed_time(e) for s, e in evs) / a.steps
+    attend_samples = [s.elapsed_time(e) for s, e in evs]
+    attend_ms = statistics.fmean(attend_samples)
 
     work = algorithmic_work(wl, labels)
     flops = sum(f for f, _ in work.values())
@@ -317,7 +366,8 @@ def main():
     achieved = flops / (attend_ms / 1e3) / 1e12
 
     flush = make_flush(dev)
-    cold_ms = time_events(layer.attend, 10, flush)
+    cold_samples = time_samples(layer.attend, 10, flush)
+    cold_ms = statistics.fmean(cold_samples)
     # full-attention baseline on the same GPU: every head Global, same inputs
     full = Layer(wl, [3] * wl.heads, q, k, v)
     for _ in range(3):
@@ -395,6 +445,8 @@ def main():
                                        "tflops": round(fb / (box_ms / 1e3) / 1e12, 1),
                                        "mfma_frac": round(fb / (box_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
         del q3, k3, v3, ws
+        torch.cuda.empty_cache()
+        extra["ceilings"] = ceilings(dev)
 
     cpu = None
     if not a.no_cpu:
@@ -424,6 +476,8 @@ def main():
                      "algorithmic_bytes": sum(b for _, b in work.values()),
                      "algorithmic_flops": flops},
         "attend_cold_ms": round(cold_ms, 4),
+        "attend_ms_stats": {"warm": summary(attend_samples), "cold": summary(cold_samples)},
+        "device": device_info(0),
         "full_attention": {"ms": round(full_ms, 4), "ms_cold": round(full_cold_ms, 4),
                            "tflops": round(full_flops / (full_ms / 1e3) / 1e12, 1),
                            "speedup_vs_full": round(full_ms / attend_ms, 3)},
