@@ -43,6 +43,8 @@ What is computed
   * Cache restructure ([Pith] "What carries the argument"; [Abs]): the
     monolithic cache is split per head: Sink and Dummy keep one block, Global
     the full sliding window, Spatial the full window stored cell by cell.
+  * fp8 KV variant: K and V cached as OCP E4M3 codes with a per-cache scale
+    (round to nearest even, saturating); attention runs on the decoded values.
 
 Pins: every function here is checked by the `not gpu` tests against closed
 forms, invariants, library routines (torch SDPA in float64, numpy.percentile)
@@ -480,6 +482,63 @@ class CacheModel:
             else:
                 raise ValueError(label)
         return data, valid
+
+
+# ----------------------------------------------------------------------------
+# fp8 KV cache variant.  The review page ties the method's memory saving to
+# the per-archetype KV buffers ([Pith] "What carries the argument"; the
+# paper's App. C as summarised there); storing K and V as 8-bit floats halves
+# those bytes again.  Format: OCP FP8 E4M3 ("fn": 1 sign, 4 exponent bits
+# with bias 7, 3 mantissa bits, no infinities, only S.1111.111 is NaN; largest
+# finite 448, smallest subnormal 2^-9).  Encoding rounds to nearest, ties to
+# even, and saturates at +-448 (the reading adopted for out-of-range values).
+# A cached value is code(fp32(x * fp32(1/scale))) with a per-cache scale for
+# K and one for V; attention then runs on decode(code) * scale.
+# ----------------------------------------------------------------------------
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(codes):
+    """uint8 E4M3 codes -> float64 values (NaN for 0x7F / 0xFF)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return sign * mag
+
+
+def e4m3_encode(x):
+    """float32 values -> uint8 E4M3 codes: round to nearest even, saturate.
+
+    With |x| = a clamped to 448: below the smallest normal 2^-6 the grid
+    step is 2^-9 and the code is round(a / 2^-9) (0..8; 8 is the smallest
+    normal's code).  From 2^e (e >= -6) up to 2^(e+1) the step is 2^(e-3)
+    and the code is 8*(e+6) + round(a / 2^(e-3)); a round-up to 16 steps
+    carries into the next binade by the same formula."""
+    x = np.asarray(x, dtype=np.float64)
+    if np.isnan(x).any():
+        raise ValueError("E4M3 encoding of NaN is not defined here (inputs must be finite)")
+    a = np.minimum(np.abs(x), E4M3_MAX)
+    sub = a < 2.0 ** -6
+    _, k = np.frexp(np.where(sub, 1.0, a))          # a = f * 2^k, f in [0.5, 1)
+    e = k - 1
+    code = np.where(sub, np.rint(a / 2.0 ** -9), 8 * (e + 6) + np.rint(a / np.exp2(e - 3.0)))
+    code = code.astype(np.int64) | np.where(np.signbit(x), 0x80, 0)
+    return code.astype(np.uint8)
+
+
+def quantize_kv(x, scale: float):
+    """Codes of a K or V block (float32 values): e4m3(fp32(x * fp32(1/scale)))."""
+    x32 = np.asarray(x, dtype=np.float32)
+    inv = np.float32(1.0) / np.float32(scale)
+    return e4m3_encode(x32 * inv)
+
+
+def dequantize_kv(codes, scale: float):
+    """float64 values a cached K or V code stands for: decode(code) * scale."""
+    return e4m3_decode(codes) * np.float64(np.float32(scale))
 
 
 # ----------------------------------------------------------------------------

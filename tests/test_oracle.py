@@ -402,6 +402,61 @@ def test_cache_window_attention_after_slide():
     np.testing.assert_allclose(out[3], sdpa_f64(q[3], blocks[4][0][3], blocks[4][1][3], full, s), atol=1e-12)
 
 
+# ----------------------------------------------------------------------------- fp8 KV codes
+def _torch_e4m3(x):
+    """torch's float32 -> float8_e4m3fn conversion (round to nearest even)."""
+    return torch.from_numpy(np.asarray(x, np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_e4m3_decode_matches_torch_on_every_code():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    got = O.e4m3_decode(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(ref)) and np.isnan(got).sum() == 2   # 0x7F, 0xFF
+    assert np.array_equal(got[~np.isnan(got)], ref[~np.isnan(ref)])
+    # closed forms of the format: 1.0, the largest finite, the smallest normal and subnormal
+    assert O.e4m3_decode(np.uint8(0x38)) == 1.0 and O.e4m3_decode(np.uint8(0x7E)) == 448.0
+    assert O.e4m3_decode(np.uint8(0x08)) == 2.0 ** -6 and O.e4m3_decode(np.uint8(0x01)) == 2.0 ** -9
+
+
+def test_e4m3_encode_round_trips_and_matches_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    vals = O.e4m3_decode(codes)
+    fin = ~np.isnan(vals)
+    assert np.array_equal(O.e4m3_encode(vals[fin]), codes[fin])           # exact values (and -0) round-trip
+    grid = np.unique(vals[fin])
+    mids = (grid[:-1] + grid[1:]) / 2                                      # ties: round to even code
+    rng = np.random.default_rng(7)
+    x = np.concatenate([mids, np.nextafter(mids, np.inf), np.nextafter(mids, -np.inf),
+                        rng.uniform(-448, 448, 20000), rng.standard_normal(20000),
+                        rng.uniform(-2.0 ** -5, 2.0 ** -5, 5000)]).astype(np.float32)
+    assert np.array_equal(O.e4m3_encode(x), _torch_e4m3(x))
+
+
+def test_e4m3_encode_saturates_and_is_monotone():
+    big = np.array([448.0, 449.0, 463.9, 464.0, 1e4, 3e38], np.float32)
+    assert np.all(O.e4m3_encode(big) == 0x7E) and np.all(O.e4m3_encode(-big) == 0xFE)
+    x = np.sort(np.random.default_rng(3).uniform(-600, 600, 50000)).astype(np.float32)
+    assert np.all(np.diff(O.e4m3_decode(O.e4m3_encode(x))) >= 0)
+    # round to nearest: the error is at most half a grid step of the value's binade
+    y = x[np.abs(x) <= 448]
+    err = np.abs(O.e4m3_decode(O.e4m3_encode(y)) - y)
+    step = np.exp2(np.floor(np.log2(np.maximum(np.abs(y), 2.0 ** -6))) - 3)
+    assert np.all(err <= step / 2 + 1e-12)
+    with pytest.raises(ValueError):
+        O.e4m3_encode(np.array([np.nan], np.float32))
+
+
+def test_quantize_kv_scales():
+    x = (np.random.default_rng(5).standard_normal((3, 50, 16)) * 3).astype(np.float32)
+    assert np.array_equal(O.quantize_kv(x, 1.0), _torch_e4m3(x))
+    assert np.array_equal(O.quantize_kv(x, 4.0), _torch_e4m3(x / 4))     # power of two: exact scaling
+    c = O.quantize_kv(x, 0.3)
+    assert np.array_equal(c, _torch_e4m3(x * (np.float32(1) / np.float32(0.3))))
+    d = O.dequantize_kv(c, 0.3)
+    assert np.all(np.abs(d - x) <= np.abs(x) * 2.0 ** -4 + 2.0 ** -10 * 0.3 + 1e-7)   # relative half-step
+
+
 # ----------------------------------------------------------------------------- planted mistakes
 def test_pins_catch_planted_mistakes(monkeypatch):
     """Plant plausible mistakes in the oracle and check a pin notices each."""
