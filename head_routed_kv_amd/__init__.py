@@ -11,14 +11,15 @@ declared in include/headcast.h.  This package is its Python face:
 from __future__ import annotations
 
 from . import _native
-from ._native import (HC_BF16, HC_DUMMY, HC_FP32, HC_GLOBAL, HC_PUSH_BLOCK, HC_REPLACE_NEWEST, HC_SINK,
-                      HC_SPATIAL, HeadcastError, hc_attend, hc_cache_append, hc_cache_bytes, hc_cache_create,
+from ._native import (HC_BF16, HC_DUMMY, HC_FP32, HC_GLOBAL, HC_KV_FP8_E4M3, HC_KV_SAME, HC_PUSH_BLOCK,
+                      HC_REPLACE_NEWEST, HC_SINK, HC_SPATIAL, HeadcastError, hc_attend, hc_cache_append, hc_cache_bytes, hc_cache_create,
                       hc_cache_destroy, hc_cache_get_layout, hc_classify, hc_classify_workspace_bytes,
                       hc_default_classify_params, hc_last_error_message, hc_status_string, hc_validate_config,
                       make_config)
 
 __all__ = ["RoutedCache", "classify", "tensor_arg", "make_config", "HeadcastError", "HC_BF16", "HC_FP32",
-           "HC_SINK", "HC_DUMMY", "HC_SPATIAL", "HC_GLOBAL", "HC_PUSH_BLOCK", "HC_REPLACE_NEWEST"]
+           "HC_SINK", "HC_DUMMY", "HC_SPATIAL", "HC_GLOBAL", "HC_PUSH_BLOCK", "HC_REPLACE_NEWEST", "HC_KV_SAME",
+           "HC_KV_FP8_E4M3"]
 
 
 def _torch():

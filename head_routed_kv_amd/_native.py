@@ -16,12 +16,14 @@ HC_OK, HC_ERR_INVALID_ARG, HC_ERR_SHAPE, HC_ERR_DTYPE, HC_ERR_ALIGN = 0, -1, -2,
 HC_ERR_WORKSPACE, HC_ERR_STATE, HC_ERR_HIP, HC_ERR_UNSUPPORTED = -5, -6, -7, -8
 HC_SINK, HC_DUMMY, HC_SPATIAL, HC_GLOBAL = 0, 1, 2, 3
 HC_BF16, HC_FP32 = 0, 1
+HC_KV_SAME, HC_KV_FP8_E4M3 = 0, 1
 HC_PUSH_BLOCK, HC_REPLACE_NEWEST = 0, 1
 
 
 class hc_config(C.Structure):
     _fields_ = [(n, C.c_int32) for n in ("num_heads", "head_dim", "grid_h", "grid_w", "block_frames",
-                                         "window_frames", "cell_h", "cell_w", "dtype")] + [("softmax_scale", C.c_float)]
+                                         "window_frames", "cell_h", "cell_w", "dtype")] + \
+               [("softmax_scale", C.c_float), ("kv_format", C.c_int32), ("k_scale", C.c_float), ("v_scale", C.c_float)]
 
 
 class hc_tensor(C.Structure):
@@ -99,9 +101,9 @@ def _check(status):
 
 
 def make_config(num_heads, head_dim, grid_h, grid_w, block_frames, window_frames, cell_h=10, cell_w=10,
-                dtype=HC_BF16, softmax_scale=0.0):
+                dtype=HC_BF16, softmax_scale=0.0, kv_format=HC_KV_SAME, k_scale=0.0, v_scale=0.0):
     return hc_config(num_heads, head_dim, grid_h, grid_w, block_frames, window_frames, cell_h, cell_w, dtype,
-                     softmax_scale)
+                     softmax_scale, kv_format, k_scale, v_scale)
 
 
 def _labels_buf(labels):

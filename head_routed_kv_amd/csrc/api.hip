@@ -35,6 +35,9 @@ hc_status hip_fail(hipError_t e, const char* what) {
 }
 
 size_t elt_size(int dtype) { return dtype == HC_BF16 ? 2 : 4; }
+bool kv_fp8(const hc_config* c) { return c->kv_format == HC_KV_FP8_E4M3; }
+size_t kv_elt_size(const hc_config* c) { return kv_fp8(c) ? 1 : elt_size(c->dtype); }
+float scale_or_one(float s) { return s > 0.f ? s : 1.0f; }
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
@@ -59,6 +62,14 @@ hc_status check_config(const hc_config* c) {
                 c->head_dim);
   if (!(c->softmax_scale >= 0.f) || !std::isfinite(c->softmax_scale))
     return fail(HC_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
+  if (c->kv_format != HC_KV_SAME && c->kv_format != HC_KV_FP8_E4M3)
+    return fail(HC_ERR_INVALID_ARG, "kv_format %d is not HC_KV_SAME or HC_KV_FP8_E4M3", c->kv_format);
+  if (kv_fp8(c)) {
+    if (c->dtype != HC_BF16) return fail(HC_ERR_DTYPE, "fp8 K/V need dtype HC_BF16");
+    if (c->head_dim != 128) return fail(HC_ERR_UNSUPPORTED, "fp8 K/V are implemented for head_dim 128 only");
+    for (float sc : {c->k_scale, c->v_scale})
+      if (!(sc >= 0.f) || !std::isfinite(sc)) return fail(HC_ERR_INVALID_ARG, "k_scale and v_scale must be finite and >= 0");
+  }
   return HC_OK;
 }
 
@@ -190,7 +201,7 @@ hc_status make_layout(const hc_config* c, const int8_t* labels, Layout* L) {
     L->head_of[lab][L->count[lab]++] = (uint8_t)h;
   }
   const Geom g = geometry(c);
-  const size_t row = (size_t)c->head_dim * elt_size(c->dtype);
+  const size_t row = (size_t)c->head_dim * kv_elt_size(c);
   L->slot_bytes[HC_GLOBAL] = L->slot_bytes[HC_SPATIAL] = (size_t)g.Nk * row;
   L->slot_bytes[HC_SINK] = L->slot_bytes[HC_DUMMY] = (size_t)g.Nq * row;
   size_t off = 0;
@@ -341,6 +352,10 @@ hc_status hc_cache_append(hc_cache* c, hc_tensor k_block, hc_tensor v_block, int
   P.src_sh = k_block.stride_head * (int64_t)e;
   P.src_st = k_block.stride_token * (int64_t)e;
   P.row_bytes = cfg->head_dim * (int)e;
+  P.dst_row_bytes = cfg->head_dim * (int)kv_elt_size(cfg);
+  P.quant = kv_fp8(cfg) ? 1 : 0;
+  P.inv_k = 1.0f / scale_or_one(cfg->k_scale);
+  P.inv_v = 1.0f / scale_or_one(cfg->v_scale);
   P.rows = g.Nq;
   P.H = cfg->num_heads;
   P.T = g.T;
@@ -398,9 +413,15 @@ hc_status hc_attend(hc_cache* c, hc_tensor q, hc_out_tensor out, hipStream_t str
   P.W = cfg->window_frames;
   P.Nq = g.Nq;
   P.scale_log2 = softmax_scale(cfg) * 1.4426950408889634f;
-  const int64_t slot_elems[4] = {
-      (int64_t)(c->L.slot_bytes[0] / elt_size(cfg->dtype)), (int64_t)(c->L.slot_bytes[1] / elt_size(cfg->dtype)),
-      (int64_t)(c->L.slot_bytes[2] / elt_size(cfg->dtype)), (int64_t)(c->L.slot_bytes[3] / elt_size(cfg->dtype))};
+  P.v_scale = 1.0f;
+  if (kv_fp8(cfg)) {   // scores and outputs of the decoded codes, times the scales
+    P.kv8 = 1;
+    P.scale_log2 *= scale_or_one(cfg->k_scale);
+    P.v_scale = scale_or_one(cfg->v_scale);
+  }
+  const size_t ke = kv_elt_size(cfg);
+  const int64_t slot_elems[4] = {(int64_t)(c->L.slot_bytes[0] / ke), (int64_t)(c->L.slot_bytes[1] / ke),
+                                 (int64_t)(c->L.slot_bytes[2] / ke), (int64_t)(c->L.slot_bytes[3] / ke)};
   int units = 0;
   for (int lab : {HC_GLOBAL, HC_SINK, HC_DUMMY, HC_SPATIAL}) {
     const int n = c->L.count[lab];
@@ -504,6 +525,7 @@ hc_status hc_classify(const hc_config* cfg, const hc_classify_params* prm, hc_te
   P.W = cfg->window_frames;
   P.Nq = g.Nq;
   P.scale_log2 = softmax_scale(cfg) * 1.4426950408889634f;
+  P.v_scale = 1.0f;
   // outputs: 0 full, 1 sink, 2 dummy, 3 spatial
   const int first[3] = {0, 0, g.Nk - g.Nq};
   const int count[3] = {g.Nk, g.Nq, g.Nq};

@@ -36,6 +36,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -137,18 +138,25 @@ __device__ __forceinline__ void store_row4(void* base, int64_t off, f32x4 v) {
   }
 }
 
-template <int D, int QB, bool OUT_F32, bool GATHER>
+template <int D, int QB, bool OUT_F32, bool GATHER, bool KV8 = false>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2 / QB, 2 / QB)))
 void attn_bf16_kernel(const AttnPlan P) {
   using TL = Tile<D>;
   constexpr int QT = 32 * QB * NW;   // queries per work group
-  // The four ring buffers (K tile then V tile each); tile j lives in buffer
-  // j mod 4.  Separate objects rather than one indexed array, so every LDS
-  // address in the unrolled loop is a constant plus a per-lane offset.
+  static_assert(!KV8 || (D == 128 && QB == 1 && !GATHER), "fp8 K/V: d = 128, ranged and cell-major kinds");
+  // The bf16 ring buffers (K tile then V tile each): four, tile j in buffer
+  // j mod 4; with fp8 K/V three, tile j in buffer j mod 3, fed from a ring of
+  // three fp8 staging buffers.  Separate objects rather than one indexed
+  // array, so every LDS address in the unrolled loop is a constant plus a
+  // per-lane offset.
+  constexpr int KB8 = KTILE * D;   // fp8 K (or V) tile bytes
   __shared__ __attribute__((aligned(16))) uint8_t smem0[TL::BUF];
   __shared__ __attribute__((aligned(16))) uint8_t smem1[TL::BUF];
   __shared__ __attribute__((aligned(16))) uint8_t smem2[TL::BUF];
-  __shared__ __attribute__((aligned(16))) uint8_t smem3[TL::BUF];
+  __shared__ __attribute__((aligned(16))) uint8_t smem3[KV8 ? 16 : TL::BUF];
+  __shared__ __attribute__((aligned(16))) uint8_t stg0[KV8 ? 2 * KB8 : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t stg1[KV8 ? 2 * KB8 : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t stg2[KV8 ? 2 * KB8 : 16];
   __shared__ int s_last;
 
   const int u = blockIdx.x;
@@ -173,8 +181,9 @@ void attn_bf16_kernel(const AttnPlan P) {
     j = (rem - slot * n_cells) * P.cell_subtiles + st;
   }
   const int qh = P.head_of[ci][slot];
-  const uint16_t* __restrict__ Kb = (const uint16_t*)C.k + slot * C.kv_sh;
-  const uint16_t* __restrict__ Vb = (const uint16_t*)C.v + slot * C.kv_sh;
+  constexpr int KVE = KV8 ? 1 : 2;   // bytes per cached K/V element
+  const char* __restrict__ Kb = (const char*)C.k + slot * C.kv_sh * KVE;
+  const char* __restrict__ Vb = (const char*)C.v + slot * C.kv_sh * KVE;
   const uint16_t* __restrict__ Qb = (const uint16_t*)P.q + qh * P.q_sh;
 
   // ---- what this unit covers --------------------------------------------
@@ -218,7 +227,7 @@ void attn_bf16_kernel(const AttnPlan P) {
   // remainder sub-tile of a cell) would leave six of eight waves idle.  They
   // run their own schedule instead: waves 0-3 take query block (w & 1) and
   // every other key tile (half w >> 1), and the halves merge through LDS.
-  const bool small = QB == 1 && !is_box && qn <= 64;
+  const bool small = !KV8 && QB == 1 && !is_box && qn <= 64;
 
   // ---- this lane's query rows (one per query block) -----------------------
   int qlocal[QB], qtok[QB];
@@ -273,7 +282,7 @@ void attn_bf16_kernel(const AttnPlan P) {
   const bool short_set = kn < KTILE;
   const int rows_avail = short_set ? kn : KTILE;
   auto tile_base = [&](int it) { return short_set ? 0 : min(it * KTILE, kn - KTILE); };
-  const int64_t rowb = C.kv_st * 2;                 // bytes per key row in global memory
+  const int64_t rowb = C.kv_st * KVE;               // bytes per key row in global memory
   // Direct load i of this wave fills rows [RPI*(NW*i+wave), +RPI) of a tile; this
   // lane writes slot (lane % CPR) of row (RPI*(4*i+wave) + lane / CPR).
   int lrow[TL::LPW];
@@ -317,6 +326,42 @@ void attn_bf16_kernel(const AttnPlan P) {
     const int row = 16 * kk + 8 * q + 4 * (vg >> 1) + (vj >> 2);
     const int col = 32 * t + 16 * (vg & 1) + 4 * (vj & 3);
     return row * TL::ROWB + 16 * ((col >> 3) ^ swz_v<D>(row)) + 2 * (col & 7);
+  };
+  // fp8 K/V: lane p = 64*wave + lane moves 16-byte piece p of the K tile and
+  // of the V tile (row p / (D/16), bytes 16*(p % (D/16)); one piece per
+  // thread at d = 128) from global memory into a row-major staging buffer,
+  // and later widens the same piece to bf16 in the ring buffer, at the
+  // swizzled slots the bf16 loads would have used.  E4M3 values are exact in
+  // bf16, so the rest of the kernel is unchanged.
+  const int p8 = 64 * wave + lane;
+  const int r8 = p8 / (D / 16), c8 = p8 % (D / 16);
+  const uint32_t ofs8 = (uint32_t)(min(r8, rows_avail - 1) * rowb + 16 * c8);
+  auto load8 = [&](int lb, uint8_t* stg) {
+    const char* kt = Kc + (int64_t)(k0 + lb) * rowb;   // uniform tile base
+    const char* vt = Vc + (int64_t)(k0 + lb) * rowb;
+    const uint32_t kd = lds_addr(stg) + 1024 * wave;
+    lds_dma16(kt, ofs8, kd);
+    lds_dma16(vt, ofs8, kd + KB8);
+  };
+  auto widen = [&](const uint8_t* stg, uint8_t* buf) {
+#pragma unroll
+    for (int kv = 0; kv < 2; ++kv) {
+      const u32x4 w = *(const u32x4*)(stg + kv * KB8 + 16 * p8);
+      bf16x8 h[2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {   // bytes 4i..4i+3 -> elements 4i..4i+3 of the piece
+        const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[i], 1.0f, false);
+        const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[i], 1.0f, true);
+        h[i >> 1][4 * (i & 1) + 0] = lo[0];
+        h[i >> 1][4 * (i & 1) + 1] = lo[1];
+        h[i >> 1][4 * (i & 1) + 2] = hi[0];
+        h[i >> 1][4 * (i & 1) + 3] = hi[1];
+      }
+      const int sw = kv == 0 ? swz_k<D>(r8) : swz_v<D>(r8);
+      uint8_t* row = buf + kv * TL::KB + r8 * TL::ROWB;
+      *(bf16x8*)(row + 16 * ((2 * c8) ^ sw)) = h[0];
+      *(bf16x8*)(row + 16 * ((2 * c8 + 1) ^ sw)) = h[1];
+    }
   };
 
   // ---- main loop -------------------------------------------------------------
@@ -392,10 +437,25 @@ void attn_bf16_kernel(const AttnPlan P) {
   const bf16x8 ones8 = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f,
                         (__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
   if (!small) {
-  load_tile(0, smem0);
-  load_tile(tile_base(min(1, ntiles - 1)), smem1);
-  load_tile(tile_base(min(2, ntiles - 1)), smem2);
-  tile_barrier();   // tiles 0 and 1 are in LDS
+  if constexpr (KV8) {
+    load8(0, stg0);
+    load8(tile_base(min(1, ntiles - 1)), stg1);
+    load8(tile_base(min(2, ntiles - 1)), stg2);
+    asm volatile("s_waitcnt vmcnt(2)" ::: "memory");   // this wave's pieces of tiles 0 and 1
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    widen(stg0, smem0);
+    widen(stg1, smem1);
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");   // tile 2 staged; widened tiles written
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    load8(tile_base(min(3, ntiles - 1)), stg0);   // every wave has read stg0
+  } else {
+    load_tile(0, smem0);
+    load_tile(tile_base(min(1, ntiles - 1)), smem1);
+    load_tile(tile_base(min(2, ntiles - 1)), smem2);
+    tile_barrier();   // tiles 0 and 1 are in LDS
+  }
   f32x16 sc[QB][2];
   scores(smem0, sc);
   // Row max of the tile in sc over both lanes of each query, computed one step
@@ -414,11 +474,12 @@ void attn_bf16_kernel(const AttnPlan P) {
 #pragma unroll
   for (int b = 0; b < QB; ++b) tmax[b] = row_max(sc[b]);
 
-  auto step = [&](const int it, const uint8_t* vbuf, const uint8_t* kbuf, uint8_t* lbuf) {
-    // Tile it+3 goes into the buffer tile it-1 left (all its reads were before
-    // the last barrier).  Active waves issue its loads between the PV MFMAs
-    // (below), where the issue costs least; idle waves issue them at once.
-    const int lb3 = tile_base(min(it + 3, ntiles - 1));
+  // One step: V of tile it and K of tile it+1 are in LDS.  `issue` starts the
+  // loads of a later tile: active waves issue them between the PV MFMAs
+  // (below), where the issue costs least; idle waves at once.  `after` runs
+  // once the PV product is issued (with fp8 K/V: widening a staged tile).
+  auto step = [&](const int it, const uint8_t* vbuf, const uint8_t* kbuf, auto issue, auto after)
+      __attribute__((always_inline)) {
     if (wave_active) {
       // Keys tile `it` must not count: rows repeated from the previous tile
       // (shifted last tile, lb + j < it*KTILE) or past a short key set.
@@ -492,7 +553,6 @@ void attn_bf16_kernel(const AttnPlan P) {
         for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
             const bf16x2 p2 = {pb[b][kk][2 * e], pb[b][kk][2 * e + 1]};
             const bf16x2 o2 = {ones8[0], ones8[1]};
             psum = __builtin_amdgcn_fdot2_f32_bf16(p2, o2, psum, false);
@@ -503,7 +563,7 @@ void attn_bf16_kernel(const AttnPlan P) {
       // feed different accumulators.
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        if (kk == 1) load_tile(lb3, lbuf);
+        if (kk == 1) issue();
 #pragma unroll
         for (int t = 0; t < D / 32; ++t) {
           typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -522,18 +582,49 @@ void attn_bf16_kernel(const AttnPlan P) {
         tmax[b] = row_max(sn[b]);
         sc[b][0] = sn[b][0], sc[b][1] = sn[b][1];
       }
+      after();
     } else {
-      load_tile(lb3, lbuf);
+      issue();
+      after();
     }
-    tile_barrier();   // tile it+2 is in LDS (all waves)
   };
-  for (int it = 0; it < ntiles; it += 4) {
-    step(it, smem0, smem1, smem3);
-    if (it + 1 < ntiles) step(it + 1, smem1, smem2, smem0);
-    if (it + 2 < ntiles) step(it + 2, smem2, smem3, smem1);
-    if (it + 3 < ntiles) step(it + 3, smem3, smem0, smem2);
+  if constexpr (KV8) {
+    // Step it widens tile it+2 (staged in stg[(it+2) mod 3]) into the bf16
+    // buffer of tile it-1, whose last reads were in the previous step, and
+    // stages tile it+4 into the buffer tile it+1 was widened from.  The
+    // barrier waits for this wave's widening writes and for all staged tiles
+    // but the newest, so tile it+3 is staged and tile it+2 widened when the
+    // next step starts.
+    auto step8 = [&](const int it, const uint8_t* vb, const uint8_t* kb, uint8_t* cb, const uint8_t* cs,
+                     uint8_t* ls) __attribute__((always_inline)) {
+      const int lb4 = tile_base(min(it + 4, ntiles - 1));
+      step(it, vb, kb, [&]() { load8(lb4, ls); }, [&]() { widen(cs, cb); });
+      asm volatile("s_waitcnt vmcnt(2) lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    };
+    for (int it = 0; it < ntiles; it += 3) {
+      step8(it, smem0, smem1, smem2, stg2, stg1);
+      if (it + 1 < ntiles) step8(it + 1, smem1, smem2, smem0, stg0, stg2);
+      if (it + 2 < ntiles) step8(it + 2, smem2, smem0, smem1, stg1, stg0);
+    }
+  } else {
+    // Tile it+3 goes into the buffer tile it-1 left (all its reads were
+    // before the last barrier).
+    auto step4 = [&](const int it, const uint8_t* vb, const uint8_t* kb, uint8_t* lb)
+        __attribute__((always_inline)) {
+      const int lb3 = tile_base(min(it + 3, ntiles - 1));
+      step(it, vb, kb, [&]() { load_tile(lb3, lb); }, []() {});
+      tile_barrier();   // tile it+2 is in LDS (all waves)
+    };
+    for (int it = 0; it < ntiles; it += 4) {
+      step4(it, smem0, smem1, smem3);
+      if (it + 1 < ntiles) step4(it + 1, smem1, smem2, smem0);
+      if (it + 2 < ntiles) step4(it + 2, smem2, smem3, smem1);
+      if (it + 3 < ntiles) step4(it + 3, smem3, smem0, smem2);
+    }
   }
-  } else if constexpr (QB == 1) {
+  } else if constexpr (QB == 1 && !KV8) {
     // ---- small units: two key halves in parallel ---------------------------
     // Pair p = tiles 2p (half 0) and 2p+1 (half 1), in buffers (0,1) for even
     // p and (2,3) for odd p; pair p+2 is loaded as soon as pair p has been
@@ -608,7 +699,6 @@ void attn_bf16_kernel(const AttnPlan P) {
         for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
             const bf16x2 p2 = {pbs[kk][2 * e], pbs[kk][2 * e + 1]};
             const bf16x2 o2 = {ones8[0], ones8[1]};
             psum = __builtin_amdgcn_fdot2_f32_bf16(p2, o2, psum, false);
@@ -740,7 +830,7 @@ void attn_bf16_kernel(const AttnPlan P) {
 #pragma unroll
         for (int i = 0; i < D / 2; ++i) acc[i] = fmaf(w, x[i], acc[i]);
       }
-      const float inv = 1.f / L;
+      const float inv = P.v_scale / L;
       const int64_t obase = (int64_t)qh * C.o_sh + (int64_t)qtok[b] * C.o_st;
 #pragma unroll
       for (int t = 0; t < D / 32; ++t)
@@ -757,7 +847,7 @@ void attn_bf16_kernel(const AttnPlan P) {
 #pragma unroll
   for (int b = 0; b < QB; ++b) {
     if (!qvalid[b]) continue;
-    const float inv = 1.f / l_tot[b];
+    const float inv = P.v_scale / l_tot[b];
     const int64_t obase = (int64_t)qh * C.o_sh + (int64_t)qtok[b] * C.o_st;
 #pragma unroll
     for (int t = 0; t < D / 32; ++t)
@@ -781,7 +871,10 @@ hipError_t launch_attn_bf16(const AttnPlan& plan, int head_dim, hipStream_t s) {
     if (gathers(plan.cat[c].kind) != gather) return hipErrorInvalidValue;  // one mode per launch
   dim3 grid(plan.total_units), block(NT);
 #define HC_LAUNCH(DD, F, G) hipLaunchKernelGGL((attn_bf16_kernel<DD, kBf16QueryBlocks, F, G>), grid, block, 0, s, plan)
-  if (head_dim == 128) {
+  if (plan.kv8) {   // fp8 K/V: d = 128, bf16 output, cache kinds only
+    if (head_dim != 128 || gather || f32) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((attn_bf16_kernel<128, kBf16QueryBlocks, false, false, true>), grid, block, 0, s, plan);
+  } else if (head_dim == 128) {
     if (gather) { if (f32) HC_LAUNCH(128, true, true); else HC_LAUNCH(128, false, true); }
     else { if (f32) HC_LAUNCH(128, true, false); else HC_LAUNCH(128, false, false); }
   } else {

@@ -73,7 +73,9 @@ struct AttnPlan {
   int64_t q_sh, q_st;
   // geometry
   int32_t T, grid_w, grid_h, cell_h, cell_w, cell_cols, B, W, Nq;
-  float scale_log2;        // softmax scale * log2(e)
+  float scale_log2;        // softmax scale * log2(e) (* the K scale of an fp8 cache)
+  float v_scale;           // output multiplier: the V scale of an fp8 cache, else 1
+  int32_t kv8;             // K/V are fp8 E4M3 codes (bf16 kernel, d = 128, cache kinds)
   // sliding-box proxy (KIND_BOX_GATHER): radius, patch rows and columns,
   // patches per frame down and across
   int32_t box_r, box_rows, box_cols_q, box_bands_y, box_bands_x;
@@ -152,7 +154,10 @@ struct AppendPlan {
   const uint8_t* k;       // source block K (bytes), head / token strides in bytes
   const uint8_t* v;
   int64_t src_sh, src_st;
-  int32_t row_bytes;      // head_dim * element size
+  int32_t row_bytes;      // source row: head_dim * element size
+  int32_t dst_row_bytes;  // cached row: row_bytes, or head_dim when quantised
+  int32_t quant;          // store bf16 rows as E4M3 codes of x * inv_k (inv_v)
+  float inv_k, inv_v;
   int32_t rows;           // B*T
   int32_t H;
   int32_t T, grid_w, grid_h, cell_h, cell_w, cell_cols, B, W;

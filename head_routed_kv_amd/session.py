@@ -21,8 +21,10 @@ window that a classifier pass reads.
 """
 from __future__ import annotations
 
-from . import (HC_GLOBAL, HC_PUSH_BLOCK, HC_REPLACE_NEWEST, HeadcastError, RoutedCache, _torch, classify,
-               torch_dtype)
+import copy
+
+from . import (HC_GLOBAL, HC_KV_SAME, HC_PUSH_BLOCK, HC_REPLACE_NEWEST, HeadcastError, RoutedCache, _torch,
+               classify, torch_dtype)
 from ._native import HC_ERR_STATE
 
 
@@ -37,7 +39,12 @@ class LayerSession:
         self.labels = None        # host list once classified
         self.diag = None          # device [H, 4] once classified
         self.blocks = 0           # blocks pushed so far
-        self.cache = RoutedCache(cfg, [HC_GLOBAL] * cfg.num_heads, device)
+        # the warm-up cache keeps K/V in the layer's dtype, since the classifier
+        # reads its window; an fp8 layout (cfg.kv_format) applies from the
+        # restructure on
+        self.warm_cfg = copy.copy(cfg)
+        self.warm_cfg.kv_format = HC_KV_SAME
+        self.cache = RoutedCache(self.warm_cfg, [HC_GLOBAL] * cfg.num_heads, device)
 
     @property
     def routed(self) -> bool:
@@ -63,7 +70,7 @@ class LayerSession:
         if self.routed:
             raise HeadcastError(HC_ERR_STATE, "the window is no longer held once the cache is restructured")
         torch = _torch()
-        cfg, lay = self.cfg, self.cache.layout()
+        cfg, lay = self.warm_cfg, self.cache.layout()
         dt = torch_dtype(cfg)
         n = cfg.num_heads * cfg.window_frames * cfg.grid_h * cfg.grid_w * cfg.head_dim
         esz = torch.tensor([], dtype=dt).element_size()

@@ -56,7 +56,7 @@ typedef enum hc_status {
   HC_OK = 0,
   HC_ERR_INVALID_ARG = -1, /* null pointer, bad enum value, bad label */
   HC_ERR_SHAPE = -2,       /* inconsistent or unsupported sizes */
-  HC_ERR_DTYPE = -3,       /* dtype not HC_BF16 / HC_FP32 */
+  HC_ERR_DTYPE = -3,       /* dtype not HC_BF16 / HC_FP32, or fp8 K/V with HC_FP32 */
   HC_ERR_ALIGN = -4,       /* pointer or stride not 16-byte aligned */
   HC_ERR_WORKSPACE = -5,   /* caller buffer smaller than required */
   HC_ERR_STATE = -6,       /* call out of order, e.g. attend before any append */
@@ -66,6 +66,7 @@ typedef enum hc_status {
 
 enum { HC_SINK = 0, HC_DUMMY = 1, HC_SPATIAL = 2, HC_GLOBAL = 3 };
 enum { HC_BF16 = 0, HC_FP32 = 1 };
+enum { HC_KV_SAME = 0, HC_KV_FP8_E4M3 = 1 };
 enum { HC_PUSH_BLOCK = 0, HC_REPLACE_NEWEST = 1 };
 
 /* Geometry and precision of one attention layer.
@@ -79,12 +80,32 @@ enum { HC_PUSH_BLOCK = 0, HC_REPLACE_NEWEST = 1 };
  *                   truncated at the frame edge
  *   dtype           HC_BF16 (MFMA path, fp32 accumulation) or HC_FP32
  *   softmax_scale   0 selects 1/sqrt(head_dim)
+ *   kv_format       how a cache stores K and V:
+ *                   HC_KV_SAME      in dtype;
+ *                   HC_KV_FP8_E4M3  as OCP FP8 E4M3 codes (1 byte), the K/V
+ *                                   memory of the per-archetype buffers
+ *                                   halved again (the review's App. C point:
+ *                                   KV bytes are the cost the restructure
+ *                                   cuts).  Needs dtype HC_BF16 (else
+ *                                   HC_ERR_DTYPE) and head_dim 128 (else
+ *                                   HC_ERR_UNSUPPORTED).  hc_cache_append
+ *                                   still takes bf16 blocks and stores
+ *                                   code(fp32(x * fp32(1/scale))), rounded to
+ *                                   nearest even and saturated at +-448
+ *                                   (inputs must be finite); hc_attend runs
+ *                                   bf16 attention on decode(code) * scale.
+ *                                   hc_classify ignores kv_format (it reads
+ *                                   the caller's bf16 window).
+ *   k_scale, v_scale  fp8 caches: positive finite scales of K and V (0
+ *                   selects 1); ignored otherwise
  * Queries are the newest block: Nq = B*T rows per head.  The window holds
  * Nk = W*T keys per head. */
 typedef struct hc_config {
   int32_t num_heads, head_dim, grid_h, grid_w, block_frames, window_frames;
   int32_t cell_h, cell_w, dtype;
   float softmax_scale;
+  int32_t kv_format;
+  float k_scale, v_scale;
 } hc_config;
 
 typedef struct hc_tensor {
@@ -131,6 +152,8 @@ typedef struct hc_cache hc_cache; /* opaque host object */
  *           cell grid) starts at row W*sum_{c'<c}|c'|; within it frame slot
  *           s = 0..W-1 holds the cell's |c| tokens in row-major (y,x) order;
  *           frame i of block b sits in frame slot (b mod (W/B))*B + i.
+ * Rows hold head_dim elements of the dtype, or head_dim bytes (E4M3 codes)
+ * in an HC_KV_FP8_E4M3 cache.
  * Rows of a ring slot that no block has reached yet are unspecified. */
 typedef struct hc_cache_layout {
   uint64_t total_bytes;
@@ -172,8 +195,9 @@ hc_status hc_cache_get_layout(const hc_cache* cache, hc_cache_layout* out);
  *                      pushed also becomes the Sink block.
  *   HC_REPLACE_NEWEST  overwrites the newest block (the K/V of the block
  *                      being denoised change every step); needs one block.
- * Spatial rows are scattered into cell-major order.  Pure data movement:
- * buffers equal the documented layout bit for bit. */
+ * Spatial rows are scattered into cell-major order.  Pure data movement
+ * (quantisation to E4M3 codes in an HC_KV_FP8_E4M3 cache): buffers equal the
+ * documented layout bit for bit. */
 hc_status hc_cache_append(hc_cache* cache, hc_tensor k_block, hc_tensor v_block, int32_t mode,
                           hipStream_t stream);
 

@@ -55,6 +55,11 @@ def test_status_strings():
     (dict(grid_h=0), N.HC_ERR_SHAPE),
     (dict(cell_w=0), N.HC_ERR_SHAPE),
     (dict(softmax_scale=-1.0), N.HC_ERR_INVALID_ARG),
+    (dict(kv_format=2), N.HC_ERR_INVALID_ARG),
+    (dict(kv_format=N.HC_KV_FP8_E4M3, dtype=N.HC_FP32), N.HC_ERR_DTYPE),
+    (dict(kv_format=N.HC_KV_FP8_E4M3, head_dim=64), N.HC_ERR_UNSUPPORTED),
+    (dict(kv_format=N.HC_KV_FP8_E4M3, k_scale=-1.0), N.HC_ERR_INVALID_ARG),
+    (dict(kv_format=N.HC_KV_FP8_E4M3, v_scale=float("inf")), N.HC_ERR_INVALID_ARG),
 ])
 def test_bad_configs(kw, err):
     c = cfg(**kw)
@@ -78,6 +83,37 @@ def test_cache_bytes_and_layout():
     assert lay.off_global_v - lay.off_global_k >= 4 * T * d * 2
     assert lay.blocks_appended == 0
     N.hc_cache_destroy(h)
+
+
+def test_fp8_cache_layout_halves_kv_bytes():
+    """An fp8 K/V cache stores one byte per element; the scales are ignored
+    unless kv_format asks for fp8, and 0 selects 1."""
+    labels = [3, 2, 0, 1]
+    c16 = cfg(k_scale=-5.0)                     # ignored: kv_format is HC_KV_SAME
+    assert N.lib().hc_validate_config(C.byref(c16)) == N.HC_OK
+    c8 = cfg(kv_format=N.HC_KV_FP8_E4M3)
+    assert N.lib().hc_validate_config(C.byref(c8)) == N.HC_OK
+    h16 = N.hc_cache_create(c16, labels, FAKE, N.hc_cache_bytes(c16, labels))
+    h8 = N.hc_cache_create(c8, labels, FAKE, N.hc_cache_bytes(c8, labels))
+    a, b = N.hc_cache_get_layout(h16), N.hc_cache_get_layout(h8)
+    T, d = 96, 128
+    assert a.off_global_v - a.off_global_k == 4 * T * d * 2
+    assert b.off_global_v - b.off_global_k == 4 * T * d
+    assert b.off_sink_v - b.off_sink_k == T * d
+    N.hc_cache_destroy(h16)
+    N.hc_cache_destroy(h8)
+    # the 720p routed layer: the K/V region (everything before the split
+    # scratch) halves exactly; the fp32 scratch of the key splits does not
+    c720 = dict(num_heads=12, head_dim=128, grid_h=45, grid_w=80, block_frames=3, window_frames=21)
+    lab720 = [2, 0, 3, 1, 3, 2, 2, 3, 2, 2, 0, 1]
+    lays = []
+    for kvf in (N.HC_KV_SAME, N.HC_KV_FP8_E4M3):
+        c = cfg(**c720, kv_format=kvf)
+        h = N.hc_cache_create(c, lab720, FAKE, N.hc_cache_bytes(c, lab720))
+        lays.append(N.hc_cache_get_layout(h))
+        N.hc_cache_destroy(h)
+    assert lays[1].off_scratch * 2 == lays[0].off_scratch == 331_776_000
+    assert lays[1].scratch_bytes == lays[0].scratch_bytes
 
 
 def test_cache_create_errors():
