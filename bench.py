@@ -64,10 +64,11 @@ def gen_inputs(wl, seed, device):
 class Layer:
     """One layer's restructured cache plus its inputs."""
 
-    def __init__(self, wl, labels, q, k, v):
+    def __init__(self, wl, labels, q, k, v, kv_format=0):
         import head_routed_kv_amd as hk
         self.hk = hk
-        cfg = hk.make_config(wl.heads, wl.head_dim, wl.grid_h, wl.grid_w, wl.block_frames, wl.window_frames)
+        cfg = hk.make_config(wl.heads, wl.head_dim, wl.grid_h, wl.grid_w, wl.block_frames, wl.window_frames,
+                             kv_format=kv_format)
         self.cache = hk.RoutedCache(cfg, [int(x) for x in labels])
         BT = wl.Nq
         for b in range(wl.n_blocks):
@@ -396,6 +397,36 @@ def main():
                            "hbm_gbs": round(by / (ms / 1e3) / 1e9, 1), "hbm_frac": round(by / (ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4)}
             del lay
         extra["rollout"] = rollout_costs(wl, labels, q, k, v, full_ms)
+        # the same layer over an fp8 (E4M3) K/V cache: K/V bytes halve, the
+        # attention arithmetic stays bf16
+        l8 = Layer(wl, labels, q, k, v, kv_format=hk.HC_KV_FP8_E4M3)
+        for _ in range(3):
+            l8.step()
+        ms8 = time_events(l8.attend, 20)
+        ms8_cold = time_events(l8.attend, 10, flush)
+        step8 = time_events(l8.step, 10)
+        extra["fp8_kv"] = {"attend_ms": round(ms8, 4), "attend_cold_ms": round(ms8_cold, 4),
+                           "ms_per_step": round(step8, 4),
+                           "query_heads_per_s": round(wl.heads * wl.Nq / (step8 / 1e3)),
+                           "tflops": round(flops / (ms8 / 1e3) / 1e12, 1),
+                           "mfma_frac": round(flops / (ms8 / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                           "cache_bytes": l8.cache.nbytes, "cache_bytes_bf16": layer.cache.nbytes}
+        del l8
+        sp = [h for h in range(wl.heads) if int(labels[h]) == 2]
+        if sp:
+            idx = torch.tensor(sp, device=dev)
+            sub = W.small(wl, heads=len(sp))
+            ls8 = Layer(sub, [2] * len(sp), q[idx].contiguous(), k[idx].contiguous(), v[idx].contiguous(),
+                        kv_format=hk.HC_KV_FP8_E4M3)
+            for _ in range(3):
+                ls8.attend()
+            ms = time_events(ls8.attend, 10, flush)
+            f, by = work[2]
+            by8 = by - (by - 2 * 2 * sub.heads * sub.Nq * sub.head_dim) // 2   # K/V read once at 1 byte
+            extra["fp8_kv"]["spatial"] = {"heads": len(sp), "ms_cold": round(ms, 4), "hbm_bytes": by8,
+                                          "hbm_gbs": round(by8 / (ms / 1e3) / 1e9, 1),
+                                          "hbm_frac": round(by8 / (ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4)}
+            del ls8
         del layer, q, k, v
         torch.cuda.empty_cache()
         # 1080p layer
