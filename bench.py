@@ -255,13 +255,14 @@ def source_fingerprint(paths):
     return h.hexdigest()
 
 
-def counter_traffic(workload):
+def counter_traffic(workload, kv="bf16"):
     """HBM bytes per launch of the attention kernel from the committed
     rocprofv3 FETCH_SIZE / WRITE_SIZE record, scaled by its copy calibration.
     None unless the record's source fingerprint matches the sources built now
     (the counters describe a kernel that no longer exists otherwise) and it
     was taken on this workload."""
-    path = os.path.join(ROOT, "profiles", f"traffic_attn_bf16_{workload}_routed.json")
+    suffix = "" if kv == "bf16" else f"_{kv}"
+    path = os.path.join(ROOT, "profiles", f"traffic_attn_bf16_{workload}_routed{suffix}.json")
     if not os.path.exists(path):
         return None
     try:
@@ -318,6 +319,8 @@ def main():
     ap.add_argument("--percentile", type=float, default=5.0, help="classifier Spatial cosine percentile")
     ap.add_argument("--rule", type=int, default=0, choices=(0, 1), help="classifier rule")
     ap.add_argument("--radius", type=int, default=2, help="sliding-box proxy radius")
+    ap.add_argument("--kv", default="bf16", choices=("bf16", "fp8"),
+                    help="K/V cache format of the timed layer (fp8: OCP E4M3 codes, bf16 arithmetic)")
     ap.add_argument("--calibrate", action="store_true",
                     help="also run a plain 1 GiB device copy (known bytes) to scale HBM counters")
     a = ap.parse_args()
@@ -341,7 +344,8 @@ def main():
     wl = W.WORKLOADS[a.workload]
     labels = W.make_labels(wl, a.seed)
     q, k, v = gen_inputs(wl, a.seed, dev)
-    layer = Layer(wl, labels, q, k, v)
+    kvf = hk.HC_KV_FP8_E4M3 if a.kv == "fp8" else hk.HC_KV_SAME
+    layer = Layer(wl, labels, q, k, v, kv_format=kvf)
     torch.cuda.synchronize()
 
     for _ in range(a.warmup):
@@ -363,6 +367,10 @@ def main():
 
     work = algorithmic_work(wl, labels)
     flops = sum(f for f, _ in work.values())
+    qo_bytes = 2 * 2 * wl.heads * wl.Nq * wl.head_dim
+    alg_bytes = sum(b for _, b in work.values())
+    if a.kv == "fp8":   # K/V read once at one byte per element
+        alg_bytes = qo_bytes + (alg_bytes - qo_bytes) // 2
     value = wl.heads * wl.Nq / (ms_step / 1e3)
     achieved = flops / (attend_ms / 1e3) / 1e12
 
@@ -370,7 +378,7 @@ def main():
     cold_samples = time_samples(layer.attend, 10, flush)
     cold_ms = statistics.fmean(cold_samples)
     # full-attention baseline on the same GPU: every head Global, same inputs
-    full = Layer(wl, [3] * wl.heads, q, k, v)
+    full = Layer(wl, [3] * wl.heads, q, k, v, kv_format=kvf)
     for _ in range(3):
         full.attend()
     full_ms = time_events(full.attend, 10)
@@ -499,12 +507,13 @@ def main():
         "config": {"workload": f"{wl.name} routed layer", "heads": wl.heads, "head_dim": wl.head_dim,
                    "grid": [wl.grid_h, wl.grid_w], "block_frames": wl.block_frames,
                    "window_frames": wl.window_frames, "queries": wl.Nq, "keys": wl.Nk,
-                   "labels": [int(x) for x in labels], "step": "append(REPLACE_NEWEST) + attend"},
+                   "labels": [int(x) for x in labels], "step": "append(REPLACE_NEWEST) + attend",
+                   "kv_cache": "bf16" if a.kv == "bf16" else "fp8_e4m3"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": counter_traffic(a.workload),
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": counter_traffic(a.workload, a.kv),
                      "kernel": "attn_bf16_kernel", "attend_ms": round(attend_ms, 4),
                      "traffic_unit": "bytes per launch (FETCH_SIZE x2.0 + WRITE_SIZE x1.0)",
-                     "algorithmic_bytes": sum(b for _, b in work.values()),
+                     "algorithmic_bytes": alg_bytes,
                      "algorithmic_flops": flops},
         "attend_cold_ms": round(cold_ms, 4),
         "attend_ms_stats": {"warm": summary(attend_samples), "cold": summary(cold_samples)},
