@@ -8,8 +8,10 @@ import head_routed_kv_amd as hk
 from head_routed_kv_amd import workloads as W
 from oracle import headcast_oracle as O
 
-BF16_TOL = 2e-2   # max |gpu - oracle| <= BF16_TOL * rms(oracle output row), per query row
+BF16_TOL = 2e-2   # per query row and channel: |gpu - oracle| <= BF16_TOL * rms(oracle row) + u * |oracle|
 FP32_TOL = 1e-5
+BF16_U = 2.0 ** -8    # unit roundoff of the output format: a bf16 result is off by up to u * |o| by itself
+FP32_U = 2.0 ** -24
 
 
 def say(*a):
@@ -61,20 +63,25 @@ def fill_cache(wl, labels, k, v):
 
 
 def check_close(got, ref, tol, what=""):
-    """got, ref [H, rows, d].  Every query row: max |gpu - oracle| over its
-    channels <= tol * RMS of the oracle's output row.  (Measured against the
+    """got, ref [H, rows, d].  Every query row and channel c: |gpu - oracle|
+    <= tol * RMS of the oracle's output row + u * |oracle_c|, u the unit
+    roundoff of the output format (bf16 for BF16_TOL, fp32 for FP32_TOL).
+    The second term is the output's own rounding, which no result in that
+    format avoids; the first bounds the kernel's arithmetic.  (Against the
     RMS of a whole head, a correctly rounded bf16 output already misses 2e-2
     on Spatial heads, whose outputs are heavy-tailed: max|o|/RMS ~ 10.)
-    Returns the worst ratio seen."""
+    Returns the worst ratio (|err| - u|o|) / RMS seen."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert got.shape == ref.shape, (got.shape, ref.shape)
     assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    u = BF16_U if tol == BF16_TOL else FP32_U
     rms = np.sqrt(np.mean(ref ** 2, axis=-1))
-    err = np.abs(got - ref).max(axis=-1)
+    excess = np.abs(got - ref) - u * np.abs(ref)
+    err = excess.max(axis=-1)
     ratio = err / np.maximum(rms, 1e-30)
     h, r = np.unravel_index(int(np.argmax(ratio)), ratio.shape)
-    assert ratio[h, r] <= tol, (f"{what} head {h} row {r}: max abs err {err[h, r]:.3e} > {tol} * row rms "
+    assert ratio[h, r] <= tol, (f"{what} head {h} row {r}: max (abs err - u|o|) {err[h, r]:.3e} > {tol} * row rms "
                                 f"{rms[h, r]:.3e}")
     return float(ratio.max())
 
