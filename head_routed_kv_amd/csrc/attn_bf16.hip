@@ -29,6 +29,10 @@
 // i receives element i&3 of the 8-byte chunks addressed by lanes (i>>2)+4e,
 // e = 0..3), so lanes addressing 4 consecutive keys x 16 channels receive 4
 // keys of one channel each, which is the MFMA operand layout.
+//
+// A cache that stores K and V as fp8 (E4M3) codes instantiates KV8: tiles are
+// staged as fp8 by the same direct loads and widened once per work group into
+// a three-deep bf16 ring, after which the arithmetic is the bf16 path's.
 #include "hc_internal.h"
 
 namespace hc {
