@@ -234,3 +234,16 @@ def test_repeat_calls_deterministic():
     out2 = cache.attend(upload(data["q"], wl))
     torch().cuda.synchronize()
     assert np.array_equal(download_bits(out), download_bits(out2))
+
+
+def test_max_heads_every_pathway():
+    """HC_MAX_HEADS = 128 heads, labels cycling through the four pathways: the
+    per-category head tables hold every head at its slot."""
+    wl = W.Workload("maxheads", 21, 128, 64, 8, 12, 1, 3, "bf16", "uniform")
+    labels = [h % 4 for h in range(128)]
+    say("case 128 heads")
+    data, cache, out = run_window(wl, labels, seed=13)
+    lay = cache.layout()
+    assert (lay.n_sink, lay.n_dummy, lay.n_spatial, lay.n_global) == (32, 32, 32, 32)
+    assert [lay.head_slot[h] for h in range(128)] == [h // 4 for h in range(128)]
+    check_close(to_float(out), oracle_routed(wl, data, labels), BF16_TOL, "128 heads")
