@@ -39,6 +39,24 @@ def _stream():
     return _torch().cuda.current_stream().cuda_stream
 
 
+def check_tensor(t, cfg, rows, name):
+    """The library reads num_heads x rows x head_dim elements of cfg's dtype
+    through a tensor's pointer and strides; anything smaller would be read
+    out of bounds, so shape, dtype and device are checked here first."""
+    want = (cfg.num_heads, rows, cfg.head_dim)
+    if tuple(t.shape) != want:
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {want} (heads, tokens, channels)")
+    if t.dtype != torch_dtype(cfg):
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {torch_dtype(cfg)}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: a device tensor is needed, got one on {t.device}")
+    return tensor_arg(t)
+
+
+def block_rows(cfg):
+    return cfg.block_frames * cfg.grid_h * cfg.grid_w
+
+
 def torch_dtype(cfg):
     torch = _torch()
     return torch.bfloat16 if cfg.dtype == HC_BF16 else torch.float32
@@ -57,12 +75,16 @@ class RoutedCache:
         self.handle = hc_cache_create(cfg, self.labels, self.mem.data_ptr(), self.mem.numel())
 
     def append(self, k_block, v_block, mode=HC_PUSH_BLOCK):
-        hc_cache_append(self.handle, tensor_arg(k_block), tensor_arg(v_block), mode, _stream())
+        n = block_rows(self.cfg)
+        hc_cache_append(self.handle, check_tensor(k_block, self.cfg, n, "k_block"),
+                        check_tensor(v_block, self.cfg, n, "v_block"), mode, _stream())
 
     def attend(self, q_block, out=None):
+        n = block_rows(self.cfg)
+        q = check_tensor(q_block, self.cfg, n, "q_block")
         if out is None:
             out = _torch().empty_like(q_block)
-        hc_attend(self.handle, tensor_arg(q_block), tensor_arg(out), _stream())
+        hc_attend(self.handle, q, check_tensor(out, self.cfg, n, "out"), _stream())
         return out
 
     def layout(self):
@@ -92,6 +114,8 @@ def classify(cfg, q_block, k_window, v_window, params=None, workspace=None):
         workspace = torch.empty(need, dtype=torch.uint8, device=q_block.device)
     labels = torch.empty(H, dtype=torch.int8, device=q_block.device)
     diag = torch.empty(H, 4, dtype=torch.float32, device=q_block.device)
-    hc_classify(cfg, params, tensor_arg(q_block), tensor_arg(k_window), tensor_arg(v_window),
+    nw = cfg.window_frames * cfg.grid_h * cfg.grid_w
+    hc_classify(cfg, params, check_tensor(q_block, cfg, block_rows(cfg), "q_block"),
+                check_tensor(k_window, cfg, nw, "k_window"), check_tensor(v_window, cfg, nw, "v_window"),
                 workspace.data_ptr(), workspace.numel(), labels.data_ptr(), diag.data_ptr(), _stream())
     return labels, diag, workspace

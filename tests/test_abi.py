@@ -218,3 +218,22 @@ def test_split_plan_for_benchmark_layers():
     lay = N.hc_cache_get_layout(h)
     assert (lay.global_splits, lay.sink_splits, lay.dummy_splits, lay.scratch_bytes) == (1, 1, 1, 0)
     N.hc_cache_destroy(h)
+
+
+def test_binding_checks_tensors_against_the_config():
+    """The torch conveniences refuse tensors the library would read out of
+    bounds (too few tokens or heads), of the wrong dtype, or in host memory."""
+    import torch
+    import head_routed_kv_amd as hk
+    c = hk.make_config(4, 64, 8, 12, 1, 4)          # B*T = 96 rows per block
+    ok = torch.zeros(4, 96, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="shape"):
+        hk.check_tensor(torch.zeros(4, 95, 64, dtype=torch.bfloat16), c, hk.block_rows(c), "k_block")
+    with pytest.raises(ValueError, match="shape"):
+        hk.check_tensor(torch.zeros(3, 96, 64, dtype=torch.bfloat16), c, 96, "k_block")
+    with pytest.raises(ValueError, match="dtype"):
+        hk.check_tensor(ok.float(), c, 96, "q_block")
+    with pytest.raises(ValueError, match="device"):
+        hk.check_tensor(ok, c, 96, "q_block")
+    with pytest.raises(ValueError, match="contiguous channels"):
+        hk.tensor_arg(torch.zeros(4, 64, 96, dtype=torch.bfloat16).transpose(1, 2))
