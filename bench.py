@@ -450,7 +450,28 @@ def main():
         extra["1080p"] = {"ms_per_step": round(ms2, 3), "query_heads_per_s": round(wl2.heads * wl2.Nq / (ms2 / 1e3)),
                           "attend_ms": round(at2, 3), "tflops": round(f2 / (at2 / 1e3) / 1e12, 1),
                           "mfma_frac": round(f2 / (at2 / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
-        del l2, q2, k2, v2
+        del l2
+        # each 1080p pathway group alone (10 Global, 8 Sink, 6 Dummy, 16 Spatial heads)
+        work2 = algorithmic_work(wl2, lab2)
+        alone = {}
+        for lab, name in ((3, "global"), (0, "sink"), (1, "dummy"), (2, "spatial")):
+            heads = [h for h in range(wl2.heads) if int(lab2[h]) == lab]
+            if not heads:
+                continue
+            idx = torch.tensor(heads, device=dev)
+            lay = Layer(W.small(wl2, heads=len(heads)), [lab] * len(heads), q2[idx].contiguous(),
+                        k2[idx].contiguous(), v2[idx].contiguous())
+            lay.attend()
+            ms = time_events(lay.attend, 3, flush)
+            f, by = work2[lab]
+            alone[name] = {"heads": len(heads), "ms_cold": round(ms, 3),
+                           "tflops": round(f / (ms / 1e3) / 1e12, 1),
+                           "mfma_frac": round(f / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                           "hbm_gbs": round(by / (ms / 1e3) / 1e9, 1), "hbm_frac": round(by / (ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4)}
+            del lay
+            torch.cuda.empty_cache()
+        extra["1080p"]["pathways"] = alone
+        del q2, k2, v2
         torch.cuda.empty_cache()
         # one-shot classifier at the 720p shape, 40 heads (full + 3 proxy outputs, cosines, rule)
         wl3 = W.WORKLOADS["classifier720p"]
