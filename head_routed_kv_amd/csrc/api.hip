@@ -474,7 +474,8 @@ hc_status hc_classify_workspace_bytes(const hc_config* cfg, size_t* bytes) {
   const Geom g = geometry(cfg);
   const size_t o = align256((size_t)4 * cfg->num_heads * g.Nq * cfg->head_dim * sizeof(float));
   const size_t cs = align256((size_t)cfg->num_heads * 4 * g.Nq * sizeof(float));
-  *bytes = o + cs;
+  const size_t ml = align256((size_t)3 * cfg->num_heads * g.Nq * 2 * sizeof(float));
+  *bytes = o + cs + ml;
   return HC_OK;
 }
 
@@ -572,17 +573,44 @@ hc_status hc_classify(const hc_config* cfg, const hc_classify_params* prm, hc_te
   P.total_units = units;
   hipError_t err;
   if (cfg->dtype == HC_BF16) {
-    // the matrix-core kernel is specialised on gathered keys: full / sink /
-    // dummy (contiguous key ranges) in one launch, the Spatial proxy in another
+    // The Sink and Dummy proxies' keys (the window's first and last block) are
+    // part of the full output's keys, so each key is attended once: the first
+    // block, the middle blocks and the last block are three contiguous ranges,
+    // each written unnormalised with its softmax state, and a merge kernel
+    // forms the full output and the two proxies.  The matrix-core kernel is
+    // specialised on gathered keys, so the Spatial proxy is a second launch.
+    float2* ML = (float2*)((uint8_t*)workspace + align256((size_t)4 * H * g.Nq * D * sizeof(float)) +
+                           align256((size_t)H * 4 * g.Nq * sizeof(float)));
+    const int64_t rows = (int64_t)H * g.Nq;
+    AttnPlan R = P;
+    R.n_cats = 0;
+    int ru = 0;
+    auto add_range = [&](int out_plane, int first, int count, float2* ml) {
+      AttnCat C = P.cat[0];
+      C.kv_first = first;
+      C.kv_count = count;
+      C.keys_per_split = count;
+      C.o = O + out_plane * plane;
+      C.ml_out = ml;
+      C.unit_begin = ru;
+      R.cat[R.n_cats++] = C;
+      ru += H * C.units_per_head;
+    };
+    if (g.nb >= 3) add_range(0, g.Nq, g.Nk - 2 * g.Nq, ML + rows);   // middle blocks (heaviest first)
+    add_range(1, 0, g.Nq, ML);                                       // first block
+    if (g.nb >= 2) add_range(2, g.Nk - g.Nq, g.Nq, ML + 2 * rows);   // last block
+    R.total_units = ru;
     AttnPlan G = P;
-    P.n_cats = 3;
-    P.total_units = P.cat[3].unit_begin;
     G.cat[0] = G.cat[3];
     G.cat[0].unit_begin = 0;
     G.n_cats = 1;
     G.total_units = H * G.cat[0].units_per_head;
-    err = launch_attn_bf16(P, D, stream);
+    err = launch_attn_bf16(R, D, stream);
     if (err == hipSuccess) err = launch_attn_bf16(G, D, stream);
+    if (err == hipSuccess) {
+      MergePlan mp{O, ML, H, g.Nq, D, g.nb >= 3 ? 1 : 0, g.nb == 1 ? 1 : 0, P.scale_log2};
+      err = launch_merge_ranges(mp, stream);
+    }
   } else {
     err = launch_attn_f32(P, D, stream);
   }

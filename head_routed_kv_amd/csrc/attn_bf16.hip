@@ -848,10 +848,12 @@ void attn_bf16_kernel(const AttnPlan P) {
     return;
   }
 
+  const bool raw = C.ml_out != nullptr;   // unnormalised output plus the softmax state
 #pragma unroll
   for (int b = 0; b < QB; ++b) {
     if (!qvalid[b]) continue;
-    const float inv = P.v_scale / l_tot[b];
+    const float inv = raw ? 1.f : P.v_scale / l_tot[b];
+    if (raw && hi == 0) C.ml_out[(int64_t)qh * P.Nq + qtok[b]] = make_float2(m_run[b], l_tot[b]);
     const int64_t obase = (int64_t)qh * C.o_sh + (int64_t)qtok[b] * C.o_st;
 #pragma unroll
     for (int t = 0; t < D / 32; ++t)

@@ -1,7 +1,15 @@
 // Classifier reductions (HeadCast review page, "What carries the argument"
 // and the free-parameter ledger; the paper's Sec. 4.2 Eq. 2-5 as the review
-// describes them).  Given each head's full-context output and its Sink,
-// Dummy and Spatial proxy outputs:
+// describes them).
+//   merge_ranges_kernel  the Sink and Dummy proxies attend over the window's
+//                   first and last block, which the full output covers too:
+//                   the attention kernel computes the first block, the
+//                   middle blocks and the last block once each (unnormalised,
+//                   with their softmax states), and this kernel forms the
+//                   full output (all three merged) and the two proxies from
+//                   them.
+// Given each head's full-context output and its Sink, Dummy and Spatial proxy
+// outputs:
 //   cosines_kernel  one wave per (head, query): the three per-query cosines
 //                   against the full output, and the squared distance between
 //                   the full and Spatial outputs (for the MSE);
@@ -54,6 +62,50 @@ __global__ __launch_bounds__(256) void cosines_kernel(const CosPlan P) {
     out[2 * P.Nq] = den_p > 0.f ? df_p / den_p : 0.f;
     out[3 * P.Nq] = se;
   }
+}
+
+// One thread per (head, query, 4 channels).  Plane 0 holds the middle
+// blocks' unnormalised output, plane 1 the first block's, plane 2 the last
+// block's; states ml[r] = (running max of raw scores, sum of weights).
+__global__ __launch_bounds__(256) void merge_ranges_kernel(const MergePlan P) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int g4 = P.D / 4;
+  const int64_t rows = (int64_t)P.H * P.Nq;
+  if (idx >= rows * g4) return;
+  const int64_t row = idx / g4;
+  const int c = (int)(idx - row * g4) * 4;
+  const int64_t plane = rows * P.D;
+  float4* o0 = (float4*)(P.o + row * P.D + c);
+  float4* o1 = (float4*)(P.o + plane + row * P.D + c);
+  float4* o2 = (float4*)(P.o + 2 * plane + row * P.D + c);
+  const float2 s0 = P.ml[row];
+  const float4 a = *o1;
+  if (P.one_block) {   // the window's only block is first, last and all of it
+    const float inv = 1.f / s0.y;
+    const float4 r = make_float4(a.x * inv, a.y * inv, a.z * inv, a.w * inv);
+    *o0 = r;
+    *o1 = r;
+    *o2 = r;
+    return;
+  }
+  const float2 s2 = P.ml[2 * rows + row];
+  const float4 b = *o2;
+  float M = fmaxf(s0.x, s2.x);
+  float2 s1 = make_float2(-INFINITY, 0.f);
+  float4 m = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (P.has_middle) {
+    s1 = P.ml[rows + row];
+    m = *o0;
+    M = fmaxf(M, s1.x);
+  }
+  const float w0 = exp2f((s0.x - M) * P.scale_log2), w2 = exp2f((s2.x - M) * P.scale_log2);
+  const float w1 = P.has_middle ? exp2f((s1.x - M) * P.scale_log2) : 0.f;
+  const float inv = 1.f / (w0 * s0.y + w1 * s1.y + w2 * s2.y);
+  *o0 = make_float4((w0 * a.x + w1 * m.x + w2 * b.x) * inv, (w0 * a.y + w1 * m.y + w2 * b.y) * inv,
+                    (w0 * a.z + w1 * m.z + w2 * b.z) * inv, (w0 * a.w + w1 * m.w + w2 * b.w) * inv);
+  const float i0 = 1.f / s0.y, i2 = 1.f / s2.y;
+  *o1 = make_float4(a.x * i0, a.y * i0, a.z * i0, a.w * i0);
+  *o2 = make_float4(b.x * i2, b.y * i2, b.z * i2, b.w * i2);
 }
 
 // float <-> order-preserving unsigned key
@@ -156,6 +208,12 @@ __global__ __launch_bounds__(RT) void reduce_kernel(const ReducePlan P) {
 }
 
 }  // namespace
+
+hipError_t launch_merge_ranges(const MergePlan& plan, hipStream_t s) {
+  const int64_t n = (int64_t)plan.H * plan.Nq * (plan.D / 4);
+  hipLaunchKernelGGL(merge_ranges_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, plan);
+  return hipGetLastError();
+}
 
 hipError_t launch_cosines(const CosPlan& plan, hipStream_t s) {
   const int64_t waves = (int64_t)plan.H * plan.Nq;

@@ -61,6 +61,8 @@ struct AttnCat {
   int32_t* counters;      // one per (head slot, q tile) when splits > 1
   int32_t out_f32;        // output written as fp32 (else the input dtype)
   int32_t pad_;
+  float2* ml_out;         // if set: write the unnormalised O and each query's softmax state (m, l) at
+                          // ml_out[head * Nq + token] (raw scores' running max, sum of weights)
 };
 
 struct AttnPlan {
@@ -181,6 +183,19 @@ struct CosPlan {
   int32_t H, Nq, D;
 };
 hipError_t launch_cosines(const CosPlan& plan, hipStream_t s);
+
+// Classifier: merge the softmax states of the window's first block, middle
+// blocks and last block (written unnormalised into the sink, full and dummy
+// output planes) into the full, Sink and Dummy outputs, in place.
+struct MergePlan {
+  float* o;                // [4][H][Nq][D] fp32: plane 0 full, 1 sink, 2 dummy
+  const float2* ml;        // [3][H][Nq]: states of the first block, the middle, the last block
+  int32_t H, Nq, D;
+  int32_t has_middle;      // the window has more than two blocks
+  int32_t one_block;       // the window is one block: first = last, stored as the first
+  float scale_log2;
+};
+hipError_t launch_merge_ranges(const MergePlan& plan, hipStream_t s);
 
 struct ReducePlan {
   const float* c;          // [H][4][Nq]

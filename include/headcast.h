@@ -224,10 +224,18 @@ hc_status hc_classify_workspace_bytes(const hc_config* cfg, size_t* bytes);
  * Writes labels_dev[num_heads] (int8) and diag_dev[num_heads][4] =
  * {C_sink, C_dummy, C_spatial, S} (fp32), both device pointers.
  * The workspace (caller-owned device memory, 256-byte aligned) holds, in
- * this order and readable after the call:
+ * this order, each region starting at a 256-byte boundary, and readable
+ * after the call:
  *   float O[4][num_heads][Nq][d]   full, sink, dummy, spatial outputs
  *   float C[num_heads][4][Nq]      per-query cos_sink, cos_dummy, cos_spatial,
  *                                  and sum_c (o_full - o_spatial)^2
+ *   float S[3][num_heads][Nq][2]   scratch (bf16): per query, the softmax state
+ *                                  (running max of the raw scores, sum of
+ *                                  weights) over the window's first block, its
+ *                                  middle blocks and its last block; the Sink
+ *                                  and Dummy proxies' keys are attended once,
+ *                                  as part of the full output's, and the three
+ *                                  outputs are merged from these states
  * The host copies labels back once (the one synchronisation point) and then
  * builds the cache with hc_cache_create. */
 hc_status hc_classify(const hc_config* cfg, const hc_classify_params* params, hc_tensor q_block,
