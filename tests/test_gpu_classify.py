@@ -59,6 +59,28 @@ def test_classifier_small_full_compare(name, tol, dtol):
         np.testing.assert_array_equal(labels, data["labels"])
 
 
+@pytest.mark.parametrize("blocks", [1, 2])
+def test_classifier_short_windows_bf16(blocks):
+    """bf16 windows of one block (first = last = whole window: Sink, Dummy and
+    full outputs coincide, every head is Sink) and of two blocks (no middle
+    range to merge), against the oracle."""
+    wl = W.Workload(f"win{blocks}", 22 + blocks, 6, 128, 13, 23, 2, 2 * blocks, "bf16", "uniform")
+    data = W.window(wl, seed=11)
+    say("case classify bf16 window of", blocks, "blocks")
+    labels, diag, outs, cos = run_classify(wl, data)
+    for h in range(wl.heads):
+        o_outs, o_diag, o_cos, _, o_lab, margin = oracle_head(wl, data, h)
+        for p in range(4):
+            check_close(outs[p, h].cpu().numpy()[None], o_outs[p][None], BF16_TOL, f"{blocks} blocks head {h} output {p}")
+        np.testing.assert_allclose(cos[h, :3].cpu().numpy(), o_cos, atol=1e-2)
+        np.testing.assert_allclose(diag[h], o_diag, atol=1e-2)
+        if margin > 0.1:
+            assert labels[h] == o_lab, (h, labels[h], o_lab, o_diag)
+    if blocks == 1:
+        assert torch().equal(outs[0], outs[1]) and torch().equal(outs[0], outs[2])
+        assert np.all(labels == O.SINK)
+
+
 @pytest.mark.parametrize("name,radius", [("tiny", 2), ("planted-small", 2), ("planted-small", 1), ("d64", 3)])
 def test_classifier_sliding_box_proxy(name, radius):
     """spatial_proxy 1: the Spatial proxy is the (2r+1)^2 box around each
