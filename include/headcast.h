@@ -30,6 +30,17 @@
  *     ordered (same stream, or caller-side synchronisation).
  *   - The library allocates no device memory: caches live in caller-owned
  *     device buffers, the classifier uses a caller-owned workspace.
+ *   - Stream capture: the enqueuing calls launch kernels only (no
+ *     allocation, copy, memset or synchronisation), so they may be recorded
+ *     into a HIP graph.  Kernel arguments are fixed when a call is recorded,
+ *     from the cache's host-side state, and a replay does not change that
+ *     state.  A recorded hc_attend stays valid as long as min(blocks pushed,
+ *     W/B) is unchanged, so once the window is full it stays valid for good.
+ *     A recorded hc_cache_append writes the block slot that was newest
+ *     (HC_REPLACE_NEWEST) or next (HC_PUSH_BLOCK) when it was recorded.  A
+ *     recorded HC_REPLACE_NEWEST + hc_attend pair, the per-step work of
+ *     denoising one block, is therefore valid until the next
+ *     HC_PUSH_BLOCK.
  *   - Tensors (hc_tensor) are per-head row-major matrices: element
  *     (head h, token t, channel c) sits at ptr + h*stride_head +
  *     t*stride_token + c, strides counted in ELEMENTS of the config's dtype.
