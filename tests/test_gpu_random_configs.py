@@ -76,3 +76,57 @@ def test_random_configuration(wl, labels, fp8, extra):
         sk, sv = W.as_float(model.sink_k, wl), W.as_float(model.sink_v, wl)
     ref = O.routed_attention(W.as_float(q, wl), fk, fv, np.array(labels), geo, k_sink=sk, v_sink=sv)
     check_close(to_float(out), ref, FP32_TOL if wl.dtype == "fp32" else BF16_TOL, wl.name)
+
+
+def draw_classifier_cases():
+    rng = np.random.default_rng(2027)
+    cases = []
+    for i in range(8):
+        d = (128, 64)[i % 2]
+        dtype = "fp32" if i % 4 == 2 else "bf16"
+        gh, gw = int(rng.integers(1, 21)), int(rng.integers(1, 33))
+        B, nb = int(rng.integers(1, 4)), int(rng.integers(1, 5))
+        ch, cw = int(rng.integers(1, 13)), int(rng.integers(1, 13))
+        H = int(rng.integers(1, 6))
+        proxy = i % 2                       # 0: the deployed cell, 1: the sliding box
+        radius = int(rng.integers(1, 4))
+        wl = W.Workload(f"rcls{i}", 60 + i, H, d, gh, gw, B, B * nb, dtype, "uniform", ch, cw)
+        cases.append(pytest.param(wl, proxy, radius, id=f"{i}-{dtype}-d{d}-{gh}x{gw}-B{B}W{B * nb}-c{ch}x{cw}-H{H}-"
+                                  + ("cell" if proxy == 0 else f"box{radius}")))
+    return cases
+
+
+@pytest.mark.parametrize("wl,proxy,radius", draw_classifier_cases())
+def test_random_classifier_configuration(wl, proxy, radius):
+    """hc_classify on a random configuration: the four outputs, the per-query
+    cosines and the per-head diagnostics against the oracle; labels where the
+    oracle's decision margin is clear of the diagnostics' tolerance."""
+    say("random classifier case", wl.name, "proxy", proxy, "radius", radius)
+    fp32 = wl.dtype == "fp32"
+    tol, dtol = (FP32_TOL, 1e-5) if fp32 else (BF16_TOL, 1e-2)
+    data = W.window(wl, seed=5)
+    t = torch()
+    q, k, v = (upload(data[n], wl) for n in ("q", "k", "v"))
+    p = hk.hc_default_classify_params()
+    p.spatial_proxy, p.radius = proxy, radius
+    labels, diag, ws = hk.classify(config(wl, False), q, k, v, p)
+    t.cuda.synchronize()
+    H, Nq, d = wl.heads, wl.Nq, wl.head_dim
+    outs = ws[:4 * H * Nq * d * 4].view(t.float32).view(4, H, Nq, d).cpu().numpy()
+    off = ((4 * H * Nq * d * 4 + 255) // 256) * 256
+    cos = ws[off:off + H * 4 * Nq * 4].view(t.float32).view(H, 4, Nq).cpu().numpy()
+    labels, diag = labels.cpu().numpy(), diag.cpu().numpy()
+
+    op = O.ClassifyParams(spatial_proxy=proxy, radius=radius)
+    geo = O.Geometry(wl.grid_h, wl.grid_w, wl.block_frames, wl.window_frames, wl.cell_h, wl.cell_w)
+    sp = O.SPATIAL if proxy == 0 else O.SLIDING
+    for h in range(H):
+        fq, fk, fv = (W.as_float(data[n], wl)[h] for n in ("q", "k", "v"))
+        o_outs = [O.attend_head(fq, fk, fv, pw, geo, radius=radius) for pw in (O.GLOBAL, O.SINK, O.DUMMY, sp)]
+        o_diag, o_cos, _ = O.head_scores(*o_outs, op)
+        for j in range(4):
+            check_close(outs[j, h][None], o_outs[j][None], tol, f"{wl.name} head {h} output {j}")
+        np.testing.assert_allclose(cos[h, :3], o_cos, atol=dtol)
+        np.testing.assert_allclose(diag[h], o_diag, atol=dtol)
+        if O.decision_margin(o_diag, op) > 10 * dtol:
+            assert labels[h] == O.decide_label(o_diag, op), (h, labels[h], o_diag)
