@@ -325,7 +325,7 @@ def main():
                     help="also run a plain 1 GiB device copy (known bytes) to scale HBM counters")
     a = ap.parse_args()
     if a.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {a.gpus}). "
+        print(f"bench.py measures one GPU: the library has no multi-GPU path (asked for --gpus {a.gpus}). "
               "Heads shard across GPUs with no exchange in attention; run one process per GPU.", file=sys.stderr)
         sys.exit(2)
 

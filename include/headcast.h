@@ -72,7 +72,7 @@ typedef enum hc_status {
   HC_ERR_WORKSPACE = -5,   /* caller buffer smaller than required */
   HC_ERR_STATE = -6,       /* call out of order, e.g. attend before any append */
   HC_ERR_HIP = -7,         /* a HIP runtime call or kernel launch failed */
-  HC_ERR_UNSUPPORTED = -8  /* valid request this build does not implement */
+  HC_ERR_UNSUPPORTED = -8  /* valid request the library does not implement */
 } hc_status;
 
 enum { HC_SINK = 0, HC_DUMMY = 1, HC_SPATIAL = 2, HC_GLOBAL = 3 };
