@@ -88,3 +88,42 @@ def test_graph_replays_of_the_block_step(kv):
     rows = sample_rows(wl, 64, seed=7)
     ref = np.stack([O.attend_head(fq[h], dk[h], dv[h], labels[h], geo, rows=rows) for h in range(wl.heads)])
     check_close(to_float(out_g)[:, rows], ref, BF16_TOL, f"graph replay {last} ({kv})")
+
+
+def test_graph_replays_of_the_classifier():
+    """hc_classify recorded once and replayed on new windows copied into the
+    recorded inputs: labels, diagnostics, the four outputs and the per-query
+    cosines equal an eager call on the same data, bit for bit."""
+    t = torch()
+    wl = W.Workload("graphcls", 31, 5, 128, 19, 29, 2, 6, "bf16", "uniform")
+    cfg = graph_config(wl, "bf16")
+    draws = [W.window(wl, seed=20 + r) for r in range(3)]
+    q_in, k_in, v_in = (upload(draws[0][n], wl) for n in ("q", "k", "v"))
+    params = hk.hc_default_classify_params()
+    ws = t.empty(hk.hc_classify_workspace_bytes(cfg), dtype=t.uint8, device="cuda")
+    hk.classify(cfg, q_in, k_in, v_in, params, ws)   # eager first call outside the recording
+    t.cuda.synchronize()
+    say("recording the classifier")
+    g = t.cuda.CUDAGraph()
+    with t.cuda.graph(g):
+        labels_g, diag_g, ws_g = hk.classify(cfg, q_in, k_in, v_in, params, ws)
+    t.cuda.synchronize()
+    for r, data in enumerate(draws):
+        say("classifier replay", r)
+        q, k, v = (upload(data[n], wl) for n in ("q", "k", "v"))
+        q_in.copy_(q)
+        k_in.copy_(k)
+        v_in.copy_(v)
+        g.replay()
+        t.cuda.synchronize()
+        got = (labels_g.clone(), diag_g.clone(), ws_g.clone())
+        labels_e, diag_e, ws_e = hk.classify(cfg, q, k, v, params)
+        t.cuda.synchronize()
+        assert t.equal(got[0], labels_e), r
+        assert t.equal(got[1], diag_e), r
+        H, Nq, d = wl.heads, wl.Nq, wl.head_dim
+        n_out = 4 * H * Nq * d * 4                      # four fp32 outputs
+        off = (n_out + 255) // 256 * 256                 # then the cosines, 256-byte aligned
+        n_cos = H * 4 * Nq * 4
+        assert t.equal(got[2][:n_out], ws_e[:n_out]), r
+        assert t.equal(got[2][off:off + n_cos], ws_e[off:off + n_cos]), r
