@@ -170,7 +170,18 @@ void attn_bf16_kernel(const AttnPlan P) {
   for (int c = 1; c < 4; ++c)
     if (c < P.n_cats && u >= P.cat[c].unit_begin) ci = c;
   const AttnCat& C = P.cat[ci];
-  const int rel = u - C.unit_begin;
+  int rel = u - C.unit_begin;
+  if (C.kind == KIND_RANGED) {
+    // Work groups reach the chip's eight XCDs round robin (block b on XCD
+    // b mod 8, each XCD taking its blocks in order), and each XCD has its own
+    // L2.  Hand every XCD a contiguous run of this category's units instead:
+    // the q tiles of one key range are consecutive units, so they then run on
+    // one or two XCDs and read the range through one or two L2s, not eight.
+    // Every XCD still gets the same number of units (to within one).
+    const int n = C.n_heads * C.units_per_head;
+    const int x = rel & 7, p = rel >> 3, q8 = n >> 3, r8 = n & 7;
+    rel = x * q8 + min(x, r8) + p;
+  }
   int slot, j;
   if (C.kind == KIND_RANGED || C.kind == KIND_BOX_GATHER) {
     slot = rel / C.units_per_head;
