@@ -45,6 +45,27 @@ def test_small_bf16_every_pathway(d):
     check_close(to_float(out), oracle_routed(wl, data, labels), BF16_TOL, f"small d{d}")
 
 
+def test_large_logits_and_late_max_jump():
+    """Q and K scaled by 4 and the window's last frame of K by 16 more (powers
+    of two: exact in bf16): scores reach a few hundred, the softmax is nearly
+    one-hot, and the running max jumps by hundreds in the last key tiles, so
+    the lazily rescaled accumulators are multiplied by exp2 of large negative
+    numbers.  Every pathway, against the oracle."""
+    wl = W.Workload("biglogit", 32, 4, 128, 23, 37, 2, 6, "bf16", "uniform")
+    labels = [3, 0, 1, 2]
+    say("case large logits")
+    data = W.window(wl, seed=13)
+    fq = W.as_float(data["q"], wl) * 4
+    fk = W.as_float(data["k"], wl) * 4
+    fk[:, -wl.T:] *= 4
+    data = dict(data, q=W.f32_to_bf16_bits(fq), k=W.f32_to_bf16_bits(fk))
+    q, k, v = (upload(data[n], wl) for n in ("q", "k", "v"))
+    cache = fill_cache(wl, labels, k, v)
+    out = cache.attend(q)
+    torch().cuda.synchronize()
+    check_close(to_float(out), oracle_routed(wl, data, labels), BF16_TOL, "large logits")
+
+
 def test_global_key_splits_merge():
     """Few queries over a long window: the cache plans several key-range
     splits for the Global head and merges them in the kernel."""
