@@ -3,7 +3,7 @@
 // over the head's key set; HeadCast review page, "What carries the
 // argument"), for fp32 layers where results must hold to fp32 accuracy.
 // Two lanes share a query (each owns half of the channels); 32-key tiles of K
-// and V are staged in LDS; softmax is online, one key at a time.
+// and V are staged in LDS; softmax is online, one tile at a time.
 #include "hc_internal.h"
 
 namespace hc {
@@ -100,26 +100,49 @@ __global__ __launch_bounds__(NT) void attn_f32_kernel(const AttnPlan P) {
       *(f32x4*)&Vs[r][4 * ch] = b;
     }
     __syncthreads();
+    // The tile's scores first, then its weights and weighted values summed
+    // within the tile, then one merge into the running state.  Every sum is a
+    // chain of at most FKT terms plus one term per tile, so rounding grows
+    // with sqrt(FKT) + sqrt(keys / FKT) instead of sqrt(keys).  Rows past the
+    // key set were loaded as zeros and are masked here.
     const int nk = min(FKT, kn - kb);
-    for (int r = 0; r < nk; ++r) {
-      if (is_box) {   // only keys within r rows and r columns of the query, on the grid
+    uint32_t keep = nk == FKT ? ~0u : (1u << nk) - 1u;   // bit r: key kb + r counts
+    if (is_box) {   // only keys within r rows and r columns of the query, on the grid
+      for (int r = 0; r < nk; ++r) {
         int f, ky, kx;
         box_pos(P, box, kb + r, f, ky, kx);
         const bool ok = ky >= 0 && ky < P.grid_h && kx >= 0 && kx < P.grid_w && abs(ky - qy) <= P.box_r &&
                         abs(kx - qx) <= P.box_r;
-        if (!ok) continue;   // the same for both lanes of a query pair
+        if (!ok) keep &= ~(1u << r);
       }
+    }
+    float s[FKT];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < FKT; ++r) {
       float dot = 0.f;
 #pragma unroll
       for (int c = 0; c < H2; ++c) dot = fmaf(q[c], Ks[r][half * H2 + c], dot);
       dot += __shfl_xor(dot, 1, 64);
-      const float s = dot * c2;
-      const float mn = fmaxf(m, s);
-      const float a = exp2f(m - mn);
-      const float p = exp2f(s - mn);
-      l = fmaf(l, a, p);
+      s[r] = (keep >> r) & 1u ? dot * c2 : -INFINITY;
+      mt = fmaxf(mt, s[r]);
+    }
+    if (mt > -INFINITY) {   // the same for both lanes of a query pair
+      float lt = 0.f, ot[H2];
 #pragma unroll
-      for (int c = 0; c < H2; ++c) o[c] = fmaf(o[c], a, p * Vs[r][half * H2 + c]);
+      for (int c = 0; c < H2; ++c) ot[c] = 0.f;
+#pragma unroll
+      for (int r = 0; r < FKT; ++r) {
+        const float p = exp2f(s[r] - mt);   // 0 for masked keys
+        lt += p;
+#pragma unroll
+        for (int c = 0; c < H2; ++c) ot[c] = fmaf(p, Vs[r][half * H2 + c], ot[c]);
+      }
+      const float mn = fmaxf(m, mt);
+      const float a = exp2f(m - mn), b = exp2f(mt - mn);
+      l = fmaf(l, a, lt * b);
+#pragma unroll
+      for (int c = 0; c < H2; ++c) o[c] = fmaf(o[c], a, ot[c] * b);
       m = mn;
     }
   }
