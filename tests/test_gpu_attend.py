@@ -66,6 +66,18 @@ def test_large_logits_and_late_max_jump():
     check_close(to_float(out), oracle_routed(wl, data, labels), BF16_TOL, "large logits")
 
 
+@pytest.mark.parametrize("d", [128, 64])
+def test_fp32_long_key_sets(d):
+    """fp32 layers with 8000-key Global sets and 1600-key Sink sets hold the
+    1e-5 bound: the fp32 kernel sums each key tile before merging it into the
+    running state, so rounding does not grow with one term per key."""
+    wl = W.Workload("f32long", 33, 3, d, 20, 40, 2, 10, "fp32", "uniform")
+    labels = [3, 0, 2]
+    say("case fp32 long key sets d", d)
+    data, cache, out = run_window(wl, labels, seed=21)
+    check_close(to_float(out), oracle_routed(wl, data, labels), FP32_TOL, f"fp32 long d{d}")
+
+
 def test_global_key_splits_merge():
     """Few queries over a long window: the cache plans several key-range
     splits for the Global head and merges them in the kernel."""
