@@ -5,7 +5,8 @@ API accepts: grids from one row or column up, cells from 1x1 to larger than
 the frame, blocks of 1-3 frames, windows of 1-5 blocks, 1-6 heads with random
 labels, d = 64 and 128, bf16 and fp32, and an fp8 cache.  Each case fills the
 window, pushes up to two more blocks (the window slides; the Sink block stays
-the first one) and attends; every output row is compared with the oracle."""
+the first one), replaces the newest block once and attends; every output row
+is compared with the oracle."""
 import numpy as np
 import pytest
 
@@ -63,6 +64,14 @@ def test_random_configuration(wl, labels, fp8, extra):
                          hk.HC_PUSH_BLOCK)
         else:
             model.append(ks[b], vs[b], hk.HC_PUSH_BLOCK)
+    # a later denoising step of the newest block replaces its keys and values
+    rk, rv = W.stream_blocks(wl, 3, 1)
+    cache.append(upload(rk[0], wl), upload(rv[0], wl), hk.HC_REPLACE_NEWEST)
+    if fp8:
+        model.append(O.quantize_kv(W.as_float(rk[0], wl), K_SCALE), O.quantize_kv(W.as_float(rv[0], wl), V_SCALE),
+                     hk.HC_REPLACE_NEWEST)
+    else:
+        model.append(rk[0], rv[0], hk.HC_REPLACE_NEWEST)
     q = W.queries(wl, 2)
     out = cache.attend(upload(q, wl))
     torch().cuda.synchronize()
