@@ -242,7 +242,7 @@ void attn_bf16_kernel(const AttnPlan P) {
   // remainder sub-tile of a cell) would leave six of eight waves idle.  They
   // run their own schedule instead: waves 0-3 take query block (w & 1) and
   // every other key tile (half w >> 1), and the halves merge through LDS.
-  const bool small = !KV8 && QB == 1 && !is_box && qn <= 64;
+  const bool small = QB == 1 && !is_box && qn <= 64;
 
   // ---- this lane's query rows (one per query block) -----------------------
   int qlocal[QB], qtok[QB];
@@ -639,12 +639,14 @@ void attn_bf16_kernel(const AttnPlan P) {
       if (it + 3 < ntiles) step4(it + 3, smem3, smem0, smem2);
     }
   }
-  } else if constexpr (QB == 1 && !KV8) {
+  } else if constexpr (QB == 1) {
     // ---- small units: two key halves in parallel ---------------------------
-    // Pair p = tiles 2p (half 0) and 2p+1 (half 1), in buffers (0,1) for even
-    // p and (2,3) for odd p; pair p+2 is loaded as soon as pair p has been
-    // read.  Not pipelined: each wave computes the scores, softmax and PV of
-    // its tile in turn.
+    // Pair p = tiles 2p (half 0) and 2p+1 (half 1).  bf16 K/V: pair p sits in
+    // buffers (0,1) for even p and (2,3) for odd p, and pair p+2 is loaded as
+    // soon as pair p has been read.  fp8 K/V: pair p is staged in two staging
+    // buffers, widened by all eight waves into buffers (0,1), and pair p+1 is
+    // staged while pair p is computed.  Not pipelined: each wave computes the
+    // scores, softmax and PV of its tile in turn.
     const int half = (wave >> 1) & 1;
     const int npairs = (ntiles + 1) >> 1;
     auto tb = [&](int t) { return tile_base(min(t, ntiles - 1)); };
@@ -657,15 +659,8 @@ void attn_bf16_kernel(const AttnPlan P) {
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
     };
-    load_tile(tb(0), smem0);
-    load_tile(tb(1), smem1);
-    load_tile(tb(2), smem2);
-    load_tile(tb(3), smem3);
-    auto pair_step = [&](const int p, uint8_t* b0, uint8_t* b1) {
-      wait_pair();
-      barrier();   // pair p is in LDS
-      const int it = 2 * p + half;
-      const uint8_t* buf = half ? b1 : b0;
+    // This wave's tile it of a pair, from the buffer buf.
+    auto tile_compute = [&](const int it, const uint8_t* buf) {
       if (wave_active && it < ntiles) {
         f32x16 st[2];
         {
@@ -732,13 +727,40 @@ void attn_bf16_kernel(const AttnPlan P) {
             oacc[0][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pbs[kk], oacc[0][t], 0, 0, 0);
           }
       }
-      barrier();   // pair p has been read by every wave
-      load_tile(tb(2 * p + 4), b0);   // pair p+2 (clamped copies past the end)
-      load_tile(tb(2 * p + 5), b1);
     };
-    for (int p = 0; p < npairs; p += 2) {
-      pair_step(p, smem0, smem1);
-      if (p + 1 < npairs) pair_step(p + 1, smem2, smem3);
+    if constexpr (!KV8) {
+      load_tile(tb(0), smem0);
+      load_tile(tb(1), smem1);
+      load_tile(tb(2), smem2);
+      load_tile(tb(3), smem3);
+      auto pair_step = [&](const int p, uint8_t* b0, uint8_t* b1) {
+        wait_pair();
+        barrier();   // pair p is in LDS
+        tile_compute(2 * p + half, half ? b1 : b0);
+        barrier();   // pair p has been read by every wave
+        load_tile(tb(2 * p + 4), b0);   // pair p+2 (clamped copies past the end)
+        load_tile(tb(2 * p + 5), b1);
+      };
+      for (int p = 0; p < npairs; p += 2) {
+        pair_step(p, smem0, smem1);
+        if (p + 1 < npairs) pair_step(p + 1, smem2, smem3);
+      }
+    } else {
+      load8(tb(0), stg0);
+      load8(tb(1), stg1);
+      for (int p = 0; p < npairs; ++p) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        barrier();   // pair p staged by every wave; every read of pair p-1 done
+        widen(stg0, smem0);
+        widen(stg1, smem1);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        barrier();   // pair p widened, and the staging buffers read, by every wave
+        if (p + 1 < npairs) {
+          load8(tb(2 * p + 2), stg0);
+          load8(tb(2 * p + 3), stg1);
+        }
+        tile_compute(2 * p + half, half ? smem1 : smem0);
+      }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     barrier();   // every LDS read and load done: the buffers are free
