@@ -41,7 +41,7 @@ def layer_flop_fraction(wl, labels):
     return sum(pairs[int(x)] for x in labels) / (len(labels) * pairs[3])
 
 
-def run(proxy=0, seed=0, workload="classifier720p_graded"):
+def run(proxy=0, seed=0, workload="classifier720p_graded", return_diag=False):
     torch = _torch()
     wl = W.WORKLOADS[workload]
     t0 = time.time()
@@ -63,21 +63,25 @@ def run(proxy=0, seed=0, workload="classifier720p_graded"):
                 p.rule, p.spatial_proxy = rule, proxy
                 p.theta_sink = p.theta_dummy = p.theta_spatial = th
                 p.theta_score = ts
-                labels, _, ws = classify(cfg, q, k, v, p, workspace=ws)
+                labels, diag, ws = classify(cfg, q, k, v, p, workspace=ws)
                 lab = labels.cpu().numpy().astype(int)
                 if rule == 0 and th == 0.95 and ts == 0.755:
                     default = lab
+                    default_diag = diag.cpu().numpy()
                 rows.append({"rule": rule, "theta": th, "theta_sc": ts, "labels": lab.tolist()})
     for r in rows:
-        lab = np.array(r.pop("labels"))
+        lab = np.array(r["labels"])
         r["counts"] = {n: int((lab == i).sum()) for i, n in enumerate(("sink", "dummy", "spatial", "global"))}
         r["flips_vs_default"] = int((lab != default).sum())
         r["differs_from_planted"] = int((lab != planted).sum())
         r["flop_fraction"] = round(layer_flop_fraction(wl, lab), 4)
-    return {"workload": f"{workload}, 40 heads, seed {seed}", "spatial_proxy": proxy,
-            "strength": [round(float(x), 3) for x in data["strength"]],
-            "planted_counts": {n: int((planted == i).sum()) for i, n in enumerate(("sink", "dummy", "spatial", "global"))},
-            "seconds": round(time.time() - t0, 1), "rows": rows}
+    out = {"workload": f"{workload}, 40 heads, seed {seed}", "spatial_proxy": proxy,
+           "strength": [round(float(x), 3) for x in data["strength"]],
+           "planted_counts": {n: int((planted == i).sum()) for i, n in enumerate(("sink", "dummy", "spatial", "global"))},
+           "seconds": round(time.time() - t0, 1), "rows": rows}
+    if return_diag:   # the default setting's [H, 4] diagnostics (they do not depend on the thresholds)
+        out["diag"] = default_diag.tolist()
+    return out
 
 
 def main():

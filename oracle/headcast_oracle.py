@@ -290,20 +290,6 @@ def percentile_linear(x, p: float) -> float:
     return float(s[lo] + (s[hi] - s[lo]) * (pos - lo))
 
 
-def classifier_outputs(q, k, v, geom: Geometry, scale: float | None = None,
-                       spatial_proxy: int = 0, radius: int = 2):
-    """The four outputs the classifier compares, each [H, Nq, d] fp64:
-    full context, Sink proxy, Dummy proxy, Spatial proxy."""
-    sp = SPATIAL if spatial_proxy == 0 else SLIDING
-    outs = {n: [] for n in ("full", "sink", "dummy", "spatial")}
-    for h in range(q.shape[0]):
-        outs["full"].append(attend_head(q[h], k[h], v[h], GLOBAL, geom, scale))
-        outs["sink"].append(attend_head(q[h], k[h], v[h], SINK, geom, scale))
-        outs["dummy"].append(attend_head(q[h], k[h], v[h], DUMMY, geom, scale))
-        outs["spatial"].append(attend_head(q[h], k[h], v[h], sp, geom, scale, radius=radius))
-    return {n: np.stack(o) for n, o in outs.items()}
-
-
 def head_scores(o_full, o_sink, o_dummy, o_spatial, params: ClassifyParams = ClassifyParams()):
     """Per-head diagnostics [C_sink, C_dummy, C_spatial, S_score] from one
     head's four outputs (each [Nq, d]), plus the per-query cosines [3, Nq]."""
@@ -339,9 +325,18 @@ def decide_label(diag, params: ClassifyParams = ClassifyParams()) -> int:
 
 
 def decision_margin(diag, params: ClassifyParams = ClassifyParams()) -> float:
-    """Smallest distance of any quantity the rule compares from the value at
-    which the decision would flip; labels are only comparable bit-for-bit
-    between two implementations when this exceeds their numeric error."""
+    """How far these diagnostics sit from a change of label.
+
+    The smallest of: the distance of each compared quantity from its
+    threshold (C_sink, C_dummy and C_spatial from theta, S from theta_sc),
+    and, under rule 0, the gap between the two largest cosines among the
+    proxies that clear.  If a second implementation's diagnostics differ from
+    these by at most eps in every component and this margin exceeds 2*eps,
+    the two take the same decision: every threshold comparison keeps its
+    outcome (gap > eps), so the same proxies clear, and the largest cleared
+    cosine stays largest (gap > 2*eps).  Quantities that cannot change the
+    label (a score gate while the cosine gate fails) still count, which
+    only makes the margin smaller than it needs to be."""
     c_sink, c_dummy, c_sp, s_sc = (float(x) for x in diag)
     gaps = [abs(c_sink - params.theta_sink), abs(c_dummy - params.theta_dummy),
             abs(c_sp - params.theta_spatial), abs(s_sc - params.theta_score)]

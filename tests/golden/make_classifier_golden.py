@@ -1,7 +1,10 @@
-"""Write the oracle's expected labels and diagnostics for the planted
-classifier workload (40 heads at the 720p shape, seed 0), with the deployed
-grid-cell Spatial proxy (default) or the sliding (2r+1)^2 box proxy
-(--spatial-proxy 1, file suffix _box).
+"""Write the oracle's expected labels and diagnostics for a planted
+classifier workload (40 heads at the 720p shape, seed 0): the planted one
+(default) or the graded one (--workload classifier720p_graded, whose
+diagnostics fix every cell of the rule and threshold study, since the
+diagnostics do not depend on the thresholds), with the deployed grid-cell
+Spatial proxy (default) or the sliding (2r+1)^2 box proxy (--spatial-proxy 1,
+file suffix _box).
 
 Calls only the CPU oracle and the seeded input generator.  Run from the
 repository root:  python tests/golden/make_classifier_golden.py [--procs N]

@@ -57,3 +57,20 @@ def test_more_than_one_gpu_is_refused(n):
                        text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+@pytest.mark.parametrize("name", ["480p", "720p", "1080p", "classifier720p"])
+def test_threshold_study_flop_fraction_matches_oracle_key_sets(name):
+    """The study's routed-FLOP fraction equals the oracle's key-set sizes
+    (pinned by brute force in the oracle tests) summed over the heads'
+    labels, over all heads Global."""
+    from head_routed_kv_amd.threshold_study import layer_flop_fraction
+    from oracle import headcast_oracle as O
+    wl = W.WORKLOADS[name]
+    g = O.Geometry(wl.grid_h, wl.grid_w, wl.block_frames, wl.window_frames, wl.cell_h, wl.cell_w)
+    rng = __import__("numpy").random.default_rng(7)
+    for _ in range(5):
+        labels = rng.integers(0, 4, wl.heads)
+        want = sum(O.keyset_sizes(g, int(x)) for x in labels) / (wl.heads * O.keyset_sizes(g, O.GLOBAL))
+        assert layer_flop_fraction(wl, labels) == pytest.approx(want, rel=1e-15)
+    assert layer_flop_fraction(wl, [3] * wl.heads) == 1.0

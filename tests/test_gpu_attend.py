@@ -6,6 +6,7 @@ import pytest
 import head_routed_kv_amd as hk
 from head_routed_kv_amd import workloads as W
 from oracle import headcast_oracle as O
+from oracle import pool
 from tests.gpu_util import (BF16_TOL, FP32_TOL, check_close, config_of, download_bits, fill_cache, geometry_of,
                             sample_rows, say, to_float, torch, upload)
 
@@ -192,26 +193,41 @@ def test_strided_token_major_inputs():
     assert torch().equal(out, ref)
 
 
-FULL = ["480p", "720p", "1080p"]
-
-
-@pytest.mark.parametrize("name", FULL)
-def test_full_size_sampled_rows(name):
-    """Full-size layer in the launch configuration the benchmark times,
-    checked on sampled query rows (oracle row by row)."""
+@pytest.mark.parametrize("name", ["480p", "720p"])
+@pytest.mark.timeout(900)   # the oracle side runs every row, process-parallel
+def test_full_size_every_row(name):
+    """The full-size layer in the launch configuration the benchmark times:
+    every query row of every head against the oracle (run process-parallel
+    over heads and row chunks)."""
     wl = W.WORKLOADS[name]
     labels = W.make_labels(wl)
-    say("case", name, "labels", labels.tolist())
+    say("case", name, "every row, labels", labels.tolist())
     data, cache, out = run_window(wl, labels)
-    rows = sample_rows(wl, 40 if name == "1080p" else 64)
+    got = to_float(out)
+    lay = cache.layout()
+    say(name, "splits", lay.global_splits, lay.sink_splits, lay.dummy_splits)
+    del data, cache, out
+    res, cpu_s, wall = pool.run(wl, 0, [(h, int(labels[h])) for h in range(wl.heads)], rows_per_task=1350)
+    say(name, f"oracle: {cpu_s:.0f} s of CPU in {wall:.0f} s")
+    ref = np.stack([res[(h, int(labels[h]))] for h in range(wl.heads)])
+    check_close(got, ref, BF16_TOL, f"{name} every row")
+
+
+@pytest.mark.timeout(900)   # the oracle side runs every row, process-parallel
+def test_1080p_every_head_sampled_rows():
+    """The 1080p layer (40 heads): every head on sampled query rows, which
+    include both ends, the frame seams and the rows of border cells."""
+    wl = W.WORKLOADS["1080p"]
+    labels = W.make_labels(wl)
+    say("case 1080p, labels", labels.tolist())
+    data, cache, out = run_window(wl, labels)
+    rows = sample_rows(wl, 40)
     got = to_float(out)[:, rows]
-    heads = range(wl.heads) if name != "1080p" else sorted(set(np.random.default_rng(1).choice(40, 12, False)))
-    heads = list(heads)
-    fq, fk, fv = (W.as_float(data[n], wl) for n in ("q", "k", "v"))
-    g = geometry_of(wl)
-    ref = np.stack([O.attend_head(fq[h], fk[h], fv[h], int(labels[h]), g, rows=rows) for h in heads])
-    worst = check_close(got[heads], ref, BF16_TOL, name)
-    say(name, "worst err/rms", worst, "splits", cache.layout().global_splits)
+    del data, cache, out
+    res, cpu_s, wall = pool.run(wl, 0, [(h, int(labels[h])) for h in range(wl.heads)], rows=rows)
+    say(f"1080p oracle: {cpu_s:.0f} s of CPU in {wall:.0f} s")
+    ref = np.stack([res[(h, int(labels[h]))] for h in range(wl.heads)])
+    check_close(got, ref, BF16_TOL, "1080p sampled rows, all heads")
 
 
 @pytest.mark.parametrize("lab", [O.GLOBAL, O.SINK, O.DUMMY, O.SPATIAL])

@@ -10,6 +10,7 @@ import pytest
 import head_routed_kv_amd as hk
 from head_routed_kv_amd import workloads as W
 from oracle import headcast_oracle as O
+from oracle import pool
 from tests.gpu_util import BF16_TOL, FP32_TOL, check_close, config_of, geometry_of, say, torch, upload
 
 pytestmark = pytest.mark.gpu
@@ -50,10 +51,11 @@ def test_classifier_small_full_compare(name, tol, dtol):
     for h in range(wl.heads):
         o_outs, o_diag, o_cos, o_mse, o_lab, margin = oracle_head(wl, data, h)
         for p in range(4):
-            check_close(outs[p, h].cpu().numpy()[None], o_outs[p][None], tol, f"{name} head {h} output {p}")
+            check_close(outs[p, h].cpu().numpy()[None], o_outs[p][None], tol, f"{name} head {h} output {p}",
+                        out_fmt="fp32")
         np.testing.assert_allclose(cos[h, :3].cpu().numpy(), o_cos, atol=dtol)
         np.testing.assert_allclose(diag[h], o_diag, atol=dtol)
-        if margin > 10 * dtol:
+        if margin > 2 * dtol:
             assert labels[h] == o_lab, (h, labels[h], o_lab, o_diag)
     if name == "planted-small":
         np.testing.assert_array_equal(labels, data["labels"])
@@ -71,10 +73,11 @@ def test_classifier_short_windows_bf16(blocks):
     for h in range(wl.heads):
         o_outs, o_diag, o_cos, _, o_lab, margin = oracle_head(wl, data, h)
         for p in range(4):
-            check_close(outs[p, h].cpu().numpy()[None], o_outs[p][None], BF16_TOL, f"{blocks} blocks head {h} output {p}")
+            check_close(outs[p, h].cpu().numpy()[None], o_outs[p][None], BF16_TOL, f"{blocks} blocks head {h} output {p}",
+                        out_fmt="fp32")
         np.testing.assert_allclose(cos[h, :3].cpu().numpy(), o_cos, atol=1e-2)
         np.testing.assert_allclose(diag[h], o_diag, atol=1e-2)
-        if margin > 0.1:
+        if margin > 2e-2:
             assert labels[h] == o_lab, (h, labels[h], o_lab, o_diag)
     if blocks == 1:
         assert torch().equal(outs[0], outs[1]) and torch().equal(outs[0], outs[2])
@@ -102,10 +105,10 @@ def test_classifier_sliding_box_proxy(name, radius):
     labels, diag, outs, cos = run_classify(wl, data, p)
     for h in range(wl.heads):
         o_outs, o_diag, o_cos, _, o_lab, margin = oracle_head(wl, data, h, op)
-        check_close(outs[3, h].cpu().numpy()[None], o_outs[3][None], tol, f"{name} head {h} box output")
+        check_close(outs[3, h].cpu().numpy()[None], o_outs[3][None], tol, f"{name} head {h} box output", out_fmt="fp32")
         np.testing.assert_allclose(cos[h, :3].cpu().numpy(), o_cos, atol=dtol)
         np.testing.assert_allclose(diag[h], o_diag, atol=dtol)
-        if margin > 10 * dtol:
+        if margin > 2 * dtol:
             assert labels[h] == o_lab, (h, labels[h], o_lab, o_diag)
 
 
@@ -122,7 +125,7 @@ def test_classifier_rule_variants_and_percentile():
     for h in range(wl.heads):
         _, o_diag, _, _, o_lab, margin = oracle_head(wl, data, h, op)
         np.testing.assert_allclose(diag[h], o_diag, atol=1e-2)
-        if margin > 0.05:
+        if margin > 2e-2:
             assert labels[h] == o_lab
 
 
@@ -131,6 +134,7 @@ def planted_720p():
     return W.window(W.WORKLOADS["classifier720p"], seed=0)
 
 
+@pytest.mark.timeout(900)   # the oracle side runs every row, process-parallel
 def test_classifier_720p_planted_golden():
     """40 planted heads at the 720p shape: labels bit-exact against the
     oracle's stored result, diagnostics within tolerance."""
@@ -140,16 +144,20 @@ def test_classifier_720p_planted_golden():
     data = planted_720p()
     say("case classify 720p planted")
     labels, diag, outs, cos = run_classify(wl, data)
-    assert min(gold["margin"]) > 1e-2
+    assert min(gold["margin"]) > 2e-2   # diagnostics within 1e-2: every label is fixed
     np.testing.assert_array_equal(labels, np.array(gold["labels"], dtype=np.int8))
     np.testing.assert_allclose(diag, np.array(gold["diag"]), atol=1e-2)
-    # spot-check the full-context output rows of two heads
-    rows = np.array([0, 5000, 10799])
-    g = geometry_of(wl)
-    for h in (0, 17):
-        fq, fk, fv = (W.as_float(data[n], wl)[h] for n in ("q", "k", "v"))
-        ref = O.attend_head(fq, fk, fv, O.GLOBAL, g, rows=rows)
-        check_close(outs[0, h].cpu().numpy()[rows][None], ref[None], BF16_TOL, f"720p full output head {h}")
+    # all four outputs, every row, of one head of each planted kind
+    planted = np.array(gold["planted"])
+    heads = [int(np.flatnonzero(planted == kind)[0]) for kind in (O.SINK, O.DUMMY, O.SPATIAL, O.GLOBAL)]
+    got = outs[:, heads].cpu().numpy()
+    del outs, cos
+    pathways = (O.GLOBAL, O.SINK, O.DUMMY, O.SPATIAL)   # workspace planes: full, sink, dummy, spatial
+    res, cpu_s, wall = pool.run(wl, 0, [(h, p) for h in heads for p in pathways], rows_per_task=1350)
+    say(f"720p classifier outputs, heads {heads}: oracle {cpu_s:.0f} s of CPU in {wall:.0f} s")
+    for j, p in enumerate(pathways):
+        ref = np.stack([res[(h, p)] for h in heads])
+        check_close(got[j], ref, BF16_TOL, f"720p planted output {j}, heads {heads}", out_fmt="fp32")
 
 
 def test_classifier_720p_planted_golden_box():
@@ -160,7 +168,7 @@ def test_classifier_720p_planted_golden_box():
     tied to the grid cells."""
     gold = json.load(open(os.path.join(GOLDEN, "classifier720p_box_seed0.json")))
     grid = json.load(open(os.path.join(GOLDEN, "classifier720p_seed0.json")))
-    assert gold["spatial_proxy"] == 1 and gold["radius"] == 2 and min(gold["margin"]) > 1e-2
+    assert gold["spatial_proxy"] == 1 and gold["radius"] == 2 and min(gold["margin"]) > 2e-2
     wl = W.WORKLOADS["classifier720p"]
     say("case classify 720p planted, sliding box")
     p = hk.hc_default_classify_params()

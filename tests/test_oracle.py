@@ -295,6 +295,76 @@ def test_rule_table(diag, rule, label):
     assert O.decide_label(diag, O.ClassifyParams(rule=rule)) == label
 
 
+# decision_margin: hand-built diagnostics, each row built so that one gap is
+# the smallest; the expected value is that gap, worked out by hand.
+@pytest.mark.parametrize("diag,rule,margin", [
+    ([0.10, 0.20, 0.30, 0.00], 0, 0.65),    # every proxy far below: the Spatial cosine gap (0.95 - 0.30)
+    ([0.96, 0.20, 0.30, 0.00], 0, 0.01),    # the Sink threshold gap
+    ([0.20, 0.93, 0.30, 0.00], 0, 0.02),    # the Dummy threshold gap, from below
+    ([0.20, 0.30, 0.97, 0.80], 0, 0.02),    # the Spatial cosine gap, from above
+    ([0.20, 0.30, 0.99, 0.76], 0, 0.005),   # the S_sc gap, from above
+    ([0.20, 0.30, 0.99, 0.745], 0, 0.01),   # the S_sc gap, from below (Spatial does not clear)
+    ([0.99, 0.98, 0.30, 0.00], 0, 0.01),    # rule 0: Sink and Dummy both clear, top-two gap
+    ([0.99, 0.98, 0.30, 0.00], 1, 0.03),    # rule 1 ignores the top-two gap: Dummy threshold gap
+    ([0.99, 0.30, 0.995, 0.90], 0, 0.005),  # rule 0: Sink and Spatial clear, top-two gap
+    ([0.99, 0.30, 0.995, 0.90], 1, 0.04),   # rule 1: Sink threshold gap
+    ([0.30, 0.985, 0.999, 0.90], 0, 0.014), # rule 0: Dummy and Spatial clear, top-two gap
+    ([0.99, 0.30, 0.999, 0.70], 0, 0.04),   # Spatial fails its score gate: no top-two gap with it
+    ([0.999, 0.99, 0.98, 0.90], 0, 0.009),  # three cleared: the top two decide (0.999 - 0.99)
+    ([0.97, 0.97, 0.30, 0.00], 0, 0.0),     # an exact tie between cleared proxies
+    ([0.95, 0.10, 0.10, 0.10], 0, 0.0),     # a cosine exactly at its (inclusive) threshold
+])
+def test_decision_margin_table(diag, rule, margin):
+    assert O.decision_margin(diag, O.ClassifyParams(rule=rule)) == pytest.approx(margin, abs=1e-12)
+
+
+def test_decision_margin_custom_thresholds():
+    p = O.ClassifyParams(theta_sink=0.5, theta_dummy=0.6, theta_spatial=0.7, theta_score=0.2)
+    assert O.decision_margin([0.55, 0.0, 0.0, 0.0], p) == pytest.approx(0.05)
+    assert O.decision_margin([0.0, 0.61, 0.0, 0.0], p) == pytest.approx(0.01)
+    assert O.decision_margin([0.0, 0.0, 0.0, 0.23], p) == pytest.approx(0.03)
+
+
+def _margin_holds(margin_fn, n=400, seed=41):
+    """Brute force: for diagnostics drawn near the thresholds, shifting every
+    component by any of -eps, 0, +eps with eps just under margin/2 never
+    changes the label (the guarantee decision_margin states)."""
+    rng = np.random.default_rng(seed)
+    shifts = np.array(np.meshgrid(*[[-1.0, 0.0, 1.0]] * 4)).reshape(4, -1).T
+    for i in range(n):
+        rule = i % 2
+        p = O.ClassifyParams(rule=rule)
+        diag = np.array([0.95, 0.95, 0.95, 0.755]) + rng.uniform(-0.05, 0.05, 4)
+        m = margin_fn(diag, p)
+        eps = 0.499 * m
+        base = O.decide_label(diag, p)
+        for s in shifts:
+            if O.decide_label(diag + eps * s, p) != base:
+                return False
+    return True
+
+
+def test_decision_margin_brute_force():
+    assert _margin_holds(O.decision_margin)
+
+
+def test_decision_margin_pins_catch_mistakes():
+    """Each plausible mistake in decision_margin fails a pin above."""
+    def no_score_gap(diag, p=O.ClassifyParams()):
+        c = [float(x) for x in diag]
+        return min(abs(c[0] - p.theta_sink), abs(c[1] - p.theta_dummy), abs(c[2] - p.theta_spatial))
+
+    def no_top_two(diag, p=O.ClassifyParams()):
+        return O.decision_margin(diag, O.ClassifyParams(rule=1))
+
+    assert not _margin_holds(no_score_gap)     # a missing gap lets the label flip inside the margin
+    assert not _margin_holds(no_top_two)
+
+    def shrunk(diag, p=O.ClassifyParams()):
+        return 0.5 * O.decision_margin(diag, p)
+    assert shrunk([0.96, 0.20, 0.30, 0.00]) != pytest.approx(0.01)   # a shrunk margin fails the table
+
+
 def test_one_block_window_classifies_sink():
     """W = B: every proxy equals the full output, cosines are 1, rule picks Sink."""
     g = O.Geometry(7, 9, 2, 2, 4, 4)
