@@ -13,11 +13,11 @@ from __future__ import annotations
 from . import _native
 from ._native import (HC_BF16, HC_DUMMY, HC_FP32, HC_GLOBAL, HC_KV_FP8_E4M3, HC_KV_SAME, HC_PUSH_BLOCK,
                       HC_REPLACE_NEWEST, HC_SINK, HC_SPATIAL, HeadcastError, hc_attend, hc_cache_append, hc_cache_bytes, hc_cache_create,
-                      hc_cache_destroy, hc_cache_get_layout, hc_classify, hc_classify_workspace_bytes,
+                      hc_cache_destroy, hc_cache_get_layout, hc_classify, hc_classify_static, hc_classify_workspace_bytes,
                       hc_default_classify_params, hc_last_error_message, hc_status_string, hc_validate_config,
                       make_config)
 
-__all__ = ["RoutedCache", "classify", "tensor_arg", "make_config", "HeadcastError", "HC_BF16", "HC_FP32",
+__all__ = ["RoutedCache", "classify", "classify_static", "tensor_arg", "make_config", "HeadcastError", "HC_BF16", "HC_FP32",
            "HC_SINK", "HC_DUMMY", "HC_SPATIAL", "HC_GLOBAL", "HC_PUSH_BLOCK", "HC_REPLACE_NEWEST", "HC_KV_SAME",
            "HC_KV_FP8_E4M3"]
 
@@ -119,3 +119,23 @@ def classify(cfg, q_block, k_window, v_window, params=None, workspace=None):
                 check_tensor(k_window, cfg, nw, "k_window"), check_tensor(v_window, cfg, nw, "v_window"),
                 workspace.data_ptr(), workspace.numel(), labels.data_ptr(), diag.data_ptr(), _stream())
     return labels, diag, workspace
+
+
+def classify_static(cfg, q_block, k_window, v_window, params=None, labels=None, diag=None):
+    """hc_classify_static: the classifier with the library's static scratch
+    as its workspace.  labels (int8 [H]) and diag (fp32 [H, 4]) device tensors
+    may be given, so that the call allocates nothing; returns them."""
+    torch = _torch()
+    params = params or hc_default_classify_params()
+    H = cfg.num_heads
+    if labels is None:
+        labels = torch.empty(H, dtype=torch.int8, device=q_block.device)
+    if diag is None:
+        diag = torch.empty(H, 4, dtype=torch.float32, device=q_block.device)
+    if labels.dtype != torch.int8 or labels.numel() < H or diag.dtype != torch.float32 or diag.numel() < 4 * H:
+        raise ValueError("labels must be int8 [num_heads] and diag fp32 [num_heads, 4]")
+    nw = cfg.window_frames * cfg.grid_h * cfg.grid_w
+    hc_classify_static(cfg, params, check_tensor(q_block, cfg, block_rows(cfg), "q_block"),
+                       check_tensor(k_window, cfg, nw, "k_window"), check_tensor(v_window, cfg, nw, "v_window"),
+                       labels.data_ptr(), diag.data_ptr(), _stream())
+    return labels, diag

@@ -60,6 +60,8 @@ EXPORTS = {
     "hc_classify_workspace_bytes": (C.c_int, [C.POINTER(hc_config), C.POINTER(C.c_size_t)]),
     "hc_classify": (C.c_int, [C.POINTER(hc_config), C.POINTER(hc_classify_params), hc_tensor, hc_tensor, hc_tensor,
                               C.c_void_p, C.c_size_t, C.c_void_p, C.c_void_p, C.c_void_p]),
+    "hc_classify_static": (C.c_int, [C.POINTER(hc_config), C.POINTER(hc_classify_params), hc_tensor, hc_tensor,
+                                     hc_tensor, C.c_void_p, C.c_void_p, C.c_void_p]),
     "hc_status_string": (C.c_char_p, [C.c_int]),
     "hc_last_error_message": (C.c_char_p, []),
 }
@@ -161,6 +163,14 @@ def hc_classify(cfg, params, q, k, v, workspace, ws_bytes, labels_dev, diag_dev,
     _check(lib().hc_classify(C.byref(cfg), C.byref(params), hc_tensor(*q), hc_tensor(*k), hc_tensor(*v),
                              C.c_void_p(workspace), ws_bytes, C.c_void_p(labels_dev), C.c_void_p(diag_dev),
                              C.c_void_p(stream)))
+
+
+def hc_classify_static(cfg, params, q, k, v, labels_dev, diag_dev, stream):
+    _check(lib().hc_classify_static(C.byref(cfg), C.byref(params), hc_tensor(*q), hc_tensor(*k), hc_tensor(*v),
+                                    C.c_void_p(labels_dev), C.c_void_p(diag_dev), C.c_void_p(stream)))
+
+
+HC_STATIC_SCRATCH_BYTES = 64 << 20
 
 
 def hc_status_string(s):

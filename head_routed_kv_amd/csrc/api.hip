@@ -1,12 +1,14 @@
 // Host side of libheadcast.so: argument checking, the restructured cache's
-// layout, work plans and kernel launches.  Allocates no device memory and
-// never synchronises the device.
+// layout, work plans and kernel launches.  Allocates no device memory (the
+// one device array it owns, the static classifier scratch, is part of the
+// loaded code object) and never synchronises the device.
 #include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
 #include <functional>
+#include <mutex>
 #include <new>
 #include <queue>
 #include <string>
@@ -479,9 +481,14 @@ hc_status hc_classify_workspace_bytes(const hc_config* cfg, size_t* bytes) {
   return HC_OK;
 }
 
-hc_status hc_classify(const hc_config* cfg, const hc_classify_params* prm, hc_tensor q, hc_tensor k_window,
-                      hc_tensor v_window, void* workspace, size_t ws_bytes, int8_t* labels_dev, float* diag_dev,
-                      hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Every check of hc_classify except those of the workspace, which the two
+// entry points bring in differently.
+hc_status check_classify(const hc_config* cfg, const hc_classify_params* prm, hc_tensor q, hc_tensor k_window,
+                         hc_tensor v_window, int8_t* labels_dev, float* diag_dev) {
   hc_status st = check_config(cfg);
   if (st) return st;
   if (!prm) return fail(HC_ERR_INVALID_ARG, "params is NULL");
@@ -497,12 +504,14 @@ hc_status hc_classify(const hc_config* cfg, const hc_classify_params* prm, hc_te
   if (k_window.stride_head != v_window.stride_head || k_window.stride_token != v_window.stride_token)
     return fail(HC_ERR_SHAPE, "k_window and v_window must share strides");
   if (!labels_dev || !diag_dev) return fail(HC_ERR_INVALID_ARG, "labels_dev / diag_dev is NULL");
-  if (!workspace) return fail(HC_ERR_INVALID_ARG, "workspace is NULL");
-  if ((uintptr_t)workspace % 256) return fail(HC_ERR_ALIGN, "workspace must be 256-byte aligned");
-  size_t need = 0;
-  hc_classify_workspace_bytes(cfg, &need);
-  if (ws_bytes < need) return fail(HC_ERR_WORKSPACE, "classifier needs %zu workspace bytes, got %zu", need, ws_bytes);
+  return HC_OK;
+}
 
+// The classifier's launches over a checked configuration and a workspace of
+// at least hc_classify_workspace_bytes.
+hc_status classify_launch(const hc_config* cfg, const hc_classify_params* prm, hc_tensor q, hc_tensor k_window,
+                          hc_tensor v_window, void* workspace, int8_t* labels_dev, float* diag_dev,
+                          hipStream_t stream) {
   const Geom g = geometry(cfg);
   const int H = cfg->num_heads, D = cfg->head_dim;
   float* O = (float*)workspace;
@@ -636,6 +645,75 @@ hc_status hc_classify(const hc_config* cfg, const hc_classify_params* prm, hc_te
   err = launch_classify_reduce(rp, stream);
   if (err != hipSuccess) return hip_fail(err, "classifier reduce launch");
   return HC_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free classifier: the workspace is this file-scope device array
+// instead of caller memory.  Host code must not use the array's name as an
+// address (it is a host-side stand-in); its device address is looked up once
+// per device and kept.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[HC_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the device that runs `stream`.
+hc_status scratch_address(hipStream_t stream, void** out) {
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  hipDevice_t dev = cur;
+  if (stream) {
+    e = hipStreamGetDevice(stream, &dev);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamGetDevice");
+  }
+  if (dev < 0 || dev >= kMaxDevices) return fail(HC_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return hip_fail(e, "hipSetDevice");
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) hipSetDevice(cur);
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p || (uintptr_t)p % 256) return fail(HC_ERR_HIP, "scratch array has no usable device address");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return HC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+hc_status hc_classify(const hc_config* cfg, const hc_classify_params* prm, hc_tensor q, hc_tensor k_window,
+                      hc_tensor v_window, void* workspace, size_t ws_bytes, int8_t* labels_dev, float* diag_dev,
+                      hipStream_t stream) {
+  hc_status st = check_classify(cfg, prm, q, k_window, v_window, labels_dev, diag_dev);
+  if (st) return st;
+  if (!workspace) return fail(HC_ERR_INVALID_ARG, "workspace is NULL");
+  if ((uintptr_t)workspace % 256) return fail(HC_ERR_ALIGN, "workspace must be 256-byte aligned");
+  size_t need = 0;
+  hc_classify_workspace_bytes(cfg, &need);
+  if (ws_bytes < need) return fail(HC_ERR_WORKSPACE, "classifier needs %zu workspace bytes, got %zu", need, ws_bytes);
+  return classify_launch(cfg, prm, q, k_window, v_window, workspace, labels_dev, diag_dev, stream);
+}
+
+hc_status hc_classify_static(const hc_config* cfg, const hc_classify_params* prm, hc_tensor q, hc_tensor k_window,
+                             hc_tensor v_window, int8_t* labels_dev, float* diag_dev, hipStream_t stream) {
+  hc_status st = check_classify(cfg, prm, q, k_window, v_window, labels_dev, diag_dev);
+  if (st) return st;
+  size_t need = 0;
+  hc_classify_workspace_bytes(cfg, &need);
+  if (need > (size_t)HC_STATIC_SCRATCH_BYTES)
+    return fail(HC_ERR_WORKSPACE, "hc_classify_static: this layer needs %zu workspace bytes, more than the %zu of "
+                "the library's static scratch; use hc_classify with a caller workspace", need,
+                (size_t)HC_STATIC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if ((st = scratch_address(stream, &ws))) return st;
+  return classify_launch(cfg, prm, q, k_window, v_window, ws, labels_dev, diag_dev, stream);
 }
 
 const char* hc_status_string(hc_status s) {

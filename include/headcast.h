@@ -29,7 +29,8 @@
  *     library never synchronises.  Calls that touch one hc_cache must be
  *     ordered (same stream, or caller-side synchronisation).
  *   - The library allocates no device memory: caches live in caller-owned
- *     device buffers, the classifier uses a caller-owned workspace.
+ *     device buffers, the classifier uses a caller-owned workspace (or, in
+ *     hc_classify_static, a static array loaded with the library).
  *   - Stream capture: the enqueuing calls launch kernels only (no
  *     allocation, copy, memset or synchronisation), so they may be recorded
  *     into a HIP graph.  Kernel arguments are fixed when a call is recorded,
@@ -252,6 +253,30 @@ hc_status hc_classify_workspace_bytes(const hc_config* cfg, size_t* bytes);
 hc_status hc_classify(const hc_config* cfg, const hc_classify_params* params, hc_tensor q_block,
                       hc_tensor k_window, hc_tensor v_window, void* workspace, size_t ws_bytes,
                       int8_t* labels_dev, float* diag_dev, hipStream_t stream);
+
+/* Bytes of the library's static classifier scratch (64 MiB; see
+ * hc_classify_static). */
+#define HC_STATIC_SCRATCH_BYTES (64u << 20)
+
+/* hc_classify for callers that cannot allocate device memory, or cannot
+ * bring a workspace: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, checks, results and
+ * kernels as hc_classify, without the workspace: the workspace is a
+ * file-scope device array of HC_STATIC_SCRATCH_BYTES inside the library,
+ * one per GPU, held from the first call on that GPU until the process ends.
+ * The call allocates nothing (no hipMalloc, no allocating library routine);
+ * its first call on a GPU looks up the array's device address there.
+ * Limit: configurations whose hc_classify_workspace_bytes exceed
+ * HC_STATIC_SCRATCH_BYTES are rejected with HC_ERR_WORKSPACE (at d = 128
+ * that is num_heads * Nq above about 32,000 query-heads).  The four proxy
+ * outputs and cosines stay in the array and are not meant to be read; only
+ * labels_dev and diag_dev are results.  Every call on one GPU shares that
+ * GPU's array: calls that overlap on one GPU (different streams, or hosts
+ * threads without ordering) race and give undefined results.  The array
+ * keeps the last call's contents; nothing in it needs to start at zero. */
+hc_status hc_classify_static(const hc_config* cfg, const hc_classify_params* params, hc_tensor q_block,
+                             hc_tensor k_window, hc_tensor v_window, int8_t* labels_dev, float* diag_dev,
+                             hipStream_t stream);
 
 const char* hc_status_string(hc_status s);
 const char* hc_last_error_message(void);

@@ -194,6 +194,33 @@ def test_classify_argument_checks():
     assert L.hc_classify(*args(p4, FAKE, need)) == N.HC_ERR_INVALID_ARG
 
 
+def test_static_classifier_rejects_layers_beyond_its_scratch():
+    """hc_classify_static checks its arguments like hc_classify and rejects a
+    layer whose workspace would not fit the static scratch, before touching
+    the GPU."""
+    L = N.lib()
+    p = N.hc_default_classify_params()
+    big = cfg(num_heads=40, grid_h=45, grid_w=80, block_frames=3, window_frames=21)   # 40-head 720p layer
+    assert N.hc_classify_workspace_bytes(big) > N.HC_STATIC_SCRATCH_BYTES
+    t = N.hc_tensor(FAKE, 75600 * 128, 128)
+    assert L.hc_classify_static(C.byref(big), C.byref(p), t, t, t, C.c_void_p(FAKE), C.c_void_p(FAKE), None) == \
+        N.HC_ERR_WORKSPACE
+    assert "static scratch" in N.hc_last_error_message()
+    small = cfg()
+    assert N.hc_classify_workspace_bytes(small) <= N.HC_STATIC_SCRATCH_BYTES
+    t = N.hc_tensor(FAKE, 384 * 128, 128)
+    p3 = N.hc_default_classify_params()
+    p3.rule = 3
+    assert L.hc_classify_static(C.byref(small), C.byref(p3), t, t, t, C.c_void_p(FAKE), C.c_void_p(FAKE), None) == \
+        N.HC_ERR_INVALID_ARG
+    assert L.hc_classify_static(C.byref(small), C.byref(p), t, t, t, None, C.c_void_p(FAKE), None) == \
+        N.HC_ERR_INVALID_ARG
+    # the header's figure and the binding's agree
+    hdr = open(HEADER).read()
+    assert re.search(r"#define HC_STATIC_SCRATCH_BYTES \(64u << 20\)", hdr)
+    assert N.HC_STATIC_SCRATCH_BYTES == 64 << 20
+
+
 def test_split_plan_for_benchmark_layers():
     """The host plans key-range splits for Global heads when their q tiles
     alone cannot fill the chip (720p: 3 Global heads x 85 q tiles)."""
