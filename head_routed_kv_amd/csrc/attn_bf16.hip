@@ -162,6 +162,7 @@ void attn_bf16_kernel(const AttnPlan P) {
   __shared__ __attribute__((aligned(16))) uint8_t stg1[KV8 ? 2 * KB8 : 16];
   __shared__ __attribute__((aligned(16))) uint8_t stg2[KV8 ? 2 * KB8 : 16];
   __shared__ int s_last;
+  __shared__ float s_ml[NW][2][64];   // small units: each wave's (m, l) for the merge
 
   const int u = blockIdx.x;
   if (u >= P.total_units) return;
@@ -240,9 +241,12 @@ void attn_bf16_kernel(const AttnPlan P) {
 
   // Units with at most 64 queries (the ragged last q tile of a head, the short
   // remainder sub-tile of a cell) would leave six of eight waves idle.  They
-  // run their own schedule instead: waves 0-3 take query block (w & 1) and
-  // every other key tile (half w >> 1), and the halves merge through LDS.
+  // run their own schedule instead, splitting the key tiles among the waves
+  // and merging the parts through LDS: bf16 K/V, all eight waves (query block
+  // w & 1, key phase w >> 1, every fourth tile); fp8 K/V, waves 0-3 (query
+  // block w & 1, every other tile).
   const bool small = QB == 1 && !is_box && qn <= 64;
+  const bool small4 = small && !KV8;
 
   // ---- this lane's query rows (one per query block) -----------------------
   int qlocal[QB], qtok[QB];
@@ -257,7 +261,7 @@ void attn_bf16_kernel(const AttnPlan P) {
       qvalid[b] = l32 < P.box_cols_q && y < P.grid_h && x < P.grid_w;
       if (qvalid[b]) qtok[b] = box.fb * P.T + y * P.grid_w + x;
     } else {
-      qvalid[b] = qlocal[b] < qn && (!small || wave < 4);
+      qvalid[b] = qlocal[b] < qn && (!small || small4 || wave < 4);
       if (qvalid[b]) qtok[b] = ranged ? (q0 + qlocal[b]) : cell_token(P, cell, q0 + qlocal[b]);
     }
     const uint16_t* qrow = Qb + (int64_t)qtok[b] * P.q_st + 8 * hi;
@@ -269,6 +273,7 @@ void attn_bf16_kernel(const AttnPlan P) {
     }
   }
   bool wave_active = is_box ? (box.py0 + wave * QB < P.grid_h)
+                   : small4 ? (32 * (wave & 1) < qn)
                    : small ? (wave < 4 && 32 * (wave & 1) < qn) : (wave * 32 * QB < qn);
   // Box proxy: bit rx of box_cm says whether this lane's query may see box
   // column rx (within r columns of it, and on the grid), shifted so that bit
@@ -374,8 +379,16 @@ void attn_bf16_kernel(const AttnPlan P) {
       }
       const int sw = kv == 0 ? swz_k<D>(r8) : swz_v<D>(r8);
       uint8_t* row = buf + kv * TL::KB + r8 * TL::ROWB;
-      *(bf16x8*)(row + 16 * ((2 * c8) ^ sw)) = h[0];
-      *(bf16x8*)(row + 16 * ((2 * c8 + 1) ^ sw)) = h[1];
+      // The piece's two slots differ in bit 0.  Each write instruction stores,
+      // per lane, the half whose slot parity is its row's parity: the 8 lanes
+      // of an even row then fill the even slots of their row and the 8 lanes
+      // of the next (odd) row its odd slots, so every 16 consecutive lanes
+      // cover all banks once.  (Writing slot 2*c8 ^ sw first sends both rows
+      // to the even slots under the V swizzle, which keeps bit 0.)
+      const int s0 = (2 * c8) ^ sw, s1 = (2 * c8 + 1) ^ sw;
+      const bool swap = (s0 & 1) != (r8 & 1);
+      *(bf16x8*)(row + 16 * (swap ? s1 : s0)) = swap ? h[1] : h[0];
+      *(bf16x8*)(row + 16 * (swap ? s0 : s1)) = swap ? h[0] : h[1];
     }
   };
 
@@ -639,22 +652,188 @@ void attn_bf16_kernel(const AttnPlan P) {
       if (it + 3 < ntiles) step4(it + 3, smem3, smem0, smem2);
     }
   }
+  } else if constexpr (QB == 1 && !KV8) {
+    // ---- small units: two query blocks x four key phases --------------------
+    // Wave w takes query block w & 1 and the key tiles ph, ph + 4, ph + 8, ...
+    // (ph = w >> 1).  The two waves of a phase stream their tiles through
+    // their own LDS buffer (K then V) and load them themselves, eight of the
+    // tile's sixteen 1 KiB pieces each (d = 128): K of round s+1 once both
+    // have read K of round s, V of round s+1 once both have read V of round
+    // s, so each load runs behind the other half of the round's math.  Three
+    // barriers per round keep the pairs in step (every wave meets every
+    // barrier; waves whose tile lies past the end skip only the math, and
+    // load a clamped copy of the last tile).
+    const int ph = wave >> 1, mem = wave & 1;
+    uint8_t* const buf = ph == 0 ? smem0 : ph == 1 ? smem1 : ph == 2 ? smem2 : smem3;
+    const int nrounds = (ntiles + 3) >> 2;
+    constexpr int PPW = TL::KB / 1024 / 2;   // 1 KiB pieces of a K (or V) tile per wave of the pair
+    auto wait_newest_part = [&]() {           // all loads but the newest PPW have landed
+      if constexpr (PPW == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    };
+    auto wait_all = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+    auto barrier = [&]() {
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    };
+    // Pieces j = 2i + mem of the K (kv = 0) or V (kv = 1) tile whose rows start
+    // at key lb: piece j holds rows RPI*j .. RPI*j + RPI - 1.
+    auto load_part = [&](const int lb, const int kv) {
+      const uint32_t dst = lds_addr(buf) + kv * TL::KB;
+      const char* base = kv ? Vc : Kc;
+      // (gathered rows: not unrolled, which keeps the row arithmetic's
+      // registers out of the pressure of the surrounding math)
+#pragma unroll(GATHER ? 1 : PPW)
+      for (int i = 0; i < PPW; ++i) {
+        const int j = 2 * i + mem;
+        const int r = TL::RPI * j + lane / TL::CPR;
+        const int slot_c = lane % TL::CPR;
+        const int lr = min(r, rows_avail - 1);
+        const int sw = kv ? swz_v<D>(r) : swz_k<D>(r);
+        if constexpr (!GATHER) {
+          lds_dma16(base + (int64_t)(k0 + lb) * rowb, (uint32_t)(lr * rowb + 16 * (slot_c ^ sw)), dst + 1024 * j);
+        } else {
+          const int tok = cell_token(P, cell, lb + lr);
+          lds_dma16_addr(base + (int64_t)tok * rowb + 16 * (slot_c ^ sw), dst + 1024 * j);
+        }
+      }
+    };
+    auto tb4 = [&](int s) { return tile_base(min(4 * s + ph, ntiles - 1)); };
+    load_part(tb4(0), 0);
+    load_part(tb4(0), 1);
+    wait_newest_part();
+    barrier();   // K of round 0 is in LDS
+    for (int s = 0; s < nrounds; ++s) {
+      const int it = 4 * s + ph;
+      const bool act = wave_active && it < ntiles;   // wave-uniform
+      const bool more = s + 1 < nrounds;             // uniform
+      f32x16 st[2];
+      if (act) {
+        f32x16 tmp[QB][2];
+        scores(buf, tmp);
+        st[0] = tmp[0][0];
+        st[1] = tmp[0][1];
+      }
+      barrier();   // both waves of each pair have read K of round s
+      if (more) load_part(tb4(s + 1), 0);
+      bf16x8 pbs[4];
+      if (act) {
+        const int lo = it * KTILE - tile_base(it);
+        const int hi_end = short_set ? kn : KTILE;
+        if (lo > 0 || hi_end < KTILE) mask_keys(st, lo, hi_end);
+        float mx = st[0][0];
+#pragma unroll
+        for (int jj = 1; jj < 16; ++jj) mx = fmaxf(mx, st[0][jj]);
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) mx = fmaxf(mx, st[1][jj]);
+        {
+          const Pair pr = halves(mx);
+          mx = fmaxf(pr.a, pr.b);
+        }
+        const bool grow = mx * c2 > fmaf(m_run[0], c2, kLazyLog2);
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+          const float m_new = grow ? mx : m_run[0];
+          const float alpha = __builtin_amdgcn_exp2f((m_run[0] - m_new) * c2);
+          l_run[0] *= alpha;
+#pragma unroll
+          for (int t = 0; t < D / 32; ++t) oacc[0][t] *= alpha;
+          m_run[0] = m_new;
+        }
+        const float mc = m_run[0] * c2;
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) {
+          st[0][jj] = __builtin_amdgcn_exp2f(fmaf(st[0][jj], c2, -mc));
+          st[1][jj] = __builtin_amdgcn_exp2f(fmaf(st[1][jj], c2, -mc));
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          pbs[0][e] = (__bf16)st[0][e];
+          pbs[1][e] = (__bf16)st[0][8 + e];
+          pbs[2][e] = (__bf16)st[1][e];
+          pbs[3][e] = (__bf16)st[1][8 + e];
+        }
+        float psum = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const bf16x2 p2 = {pbs[kk][2 * e], pbs[kk][2 * e + 1]};
+            const bf16x2 o2 = {ones8[0], ones8[1]};
+            psum = __builtin_amdgcn_fdot2_f32_bf16(p2, o2, psum, false);
+          }
+        l_run[0] += psum;
+      }
+      if (more) wait_newest_part();   // V of round s has landed (K of round s+1 may still fly)
+      else wait_all();
+      barrier();   // ... for both waves of each pair
+      if (act) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+          for (int t = 0; t < D / 32; ++t) {
+            typedef short s16x4 __attribute__((ext_vector_type(4)));
+            const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (s16x4 __attribute__((address_space(3)))*)((lds_u8*)buf + TL::KB + vt_addr(t, kk, 0)));
+            const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (s16x4 __attribute__((address_space(3)))*)((lds_u8*)buf + TL::KB + vt_addr(t, kk, 1)));
+            const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+            oacc[0][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pbs[kk], oacc[0][t], 0, 0, 0);
+          }
+      }
+      if (more) wait_all();   // K of round s+1 has landed
+      barrier();   // both waves of each pair have read V of round s; K of round s+1 is in LDS
+      if (more) load_part(tb4(s + 1), 1);
+    }
+    // Phases 1-3 hand (O, m, l) to phase 0 of the same query block: O through
+    // their own buffer (both waves of a pair: 2 x 64 floats x 64 lanes at
+    // d = 128, the buffer's size), m and l through s_ml.
+    constexpr int NV = 16 * (D / 32);
+    if (ph > 0) {
+      float* xo = (float*)buf + mem * NV * 64;
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) xo[(16 * t + i) * 64 + lane] = oacc[0][t][i];
+      s_ml[wave][0][lane] = m_run[0];
+      s_ml[wave][1][lane] = l_run[0];
+    }
+    __syncthreads();
+    if (ph == 0) {
+      float mp[4], ap[4];
+      mp[0] = m_run[0];
+#pragma unroll
+      for (int p = 1; p < 4; ++p) mp[p] = s_ml[2 * p + mem][0][lane];
+      const float M = fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3]));
+#pragma unroll
+      for (int p = 0; p < 4; ++p) ap[p] = __builtin_amdgcn_exp2f((mp[p] - M) * c2);
+      float L = l_run[0] * ap[0];
+#pragma unroll
+      for (int p = 1; p < 4; ++p) L = fmaf(s_ml[2 * p + mem][1][lane], ap[p], L);
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float o = oacc[0][t][i] * ap[0];
+          o = fmaf(((const float*)smem1)[mem * NV * 64 + (16 * t + i) * 64 + lane], ap[1], o);
+          o = fmaf(((const float*)smem2)[mem * NV * 64 + (16 * t + i) * 64 + lane], ap[2], o);
+          o = fmaf(((const float*)smem3)[mem * NV * 64 + (16 * t + i) * 64 + lane], ap[3], o);
+          oacc[0][t][i] = o;
+        }
+      l_run[0] = L;
+      m_run[0] = M;
+    }
+    wave_active = wave_active && wave < 2;
+    qvalid[0] = qvalid[0] && wave < 2;
   } else if constexpr (QB == 1) {
-    // ---- small units: two key halves in parallel ---------------------------
-    // Pair p = tiles 2p (half 0) and 2p+1 (half 1).  bf16 K/V: pair p sits in
-    // buffers (0,1) for even p and (2,3) for odd p, and pair p+2 is loaded as
-    // soon as pair p has been read.  fp8 K/V: pair p is staged in two staging
-    // buffers, widened by all eight waves into buffers (0,1), and pair p+1 is
-    // staged while pair p is computed.  Not pipelined: each wave computes the
-    // scores, softmax and PV of its tile in turn.
+    // ---- small units, fp8 K/V: two key halves in parallel -------------------
+    // Pair p = tiles 2p (half 0) and 2p+1 (half 1), computed by waves 0-3:
+    // query block w & 1, half (w >> 1) & 1.  Pair p is staged as fp8 in two
+    // staging buffers, widened by all eight waves into buffers (0,1), and
+    // pair p+1 is staged while pair p is computed.  Not pipelined: each wave
+    // computes the scores, softmax and PV of its tile in turn.
     const int half = (wave >> 1) & 1;
     const int npairs = (ntiles + 1) >> 1;
     auto tb = [&](int t) { return tile_base(min(t, ntiles - 1)); };
-    auto wait_pair = [&]() {   // all but the newest pair's 4*LPW loads have landed
-      if constexpr (4 * TL::LPW == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-      else if constexpr (4 * TL::LPW == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    };
     auto barrier = [&]() {
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
@@ -728,24 +907,7 @@ void attn_bf16_kernel(const AttnPlan P) {
           }
       }
     };
-    if constexpr (!KV8) {
-      load_tile(tb(0), smem0);
-      load_tile(tb(1), smem1);
-      load_tile(tb(2), smem2);
-      load_tile(tb(3), smem3);
-      auto pair_step = [&](const int p, uint8_t* b0, uint8_t* b1) {
-        wait_pair();
-        barrier();   // pair p is in LDS
-        tile_compute(2 * p + half, half ? b1 : b0);
-        barrier();   // pair p has been read by every wave
-        load_tile(tb(2 * p + 4), b0);   // pair p+2 (clamped copies past the end)
-        load_tile(tb(2 * p + 5), b1);
-      };
-      for (int p = 0; p < npairs; p += 2) {
-        pair_step(p, smem0, smem1);
-        if (p + 1 < npairs) pair_step(p + 1, smem2, smem3);
-      }
-    } else {
+    {
       load8(tb(0), stg0);
       load8(tb(1), stg1);
       for (int p = 0; p < npairs; ++p) {

@@ -36,7 +36,6 @@ enum : int32_t { KIND_RANGED = 0, KIND_CELL_MAJOR = 1, KIND_CELL_GATHER = 2, KIN
 
 constexpr int kBf16QueryBlocks = 1;                  // 32-query blocks per wave, bf16 kernel
 constexpr int kBf16Waves = 8;                        // waves per work group, bf16 kernel
-constexpr int kBf16GroupsPerCU = 8 / (kBf16Waves * kBf16QueryBlocks);  // 2 waves per SIMD at QB = 1
 constexpr int QTILE_BF16 = 32 * kBf16QueryBlocks * kBf16Waves;          // queries per work group, bf16 kernel
 constexpr int QTILE_F32 = 128;                       // queries per work group, fp32 kernel
 constexpr int KTILE = 64;                            // keys per inner iteration

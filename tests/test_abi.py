@@ -223,7 +223,7 @@ def test_static_classifier_rejects_layers_beyond_its_scratch():
 
 def test_split_plan_for_benchmark_layers():
     """The host plans key-range splits for Global heads when their q tiles
-    alone cannot fill the chip (720p: 3 Global heads x 85 q tiles)."""
+    alone cannot fill the chip (720p: 3 Global heads x 43 q tiles)."""
     c = N.make_config(12, 128, 45, 80, 3, 21)
     labels = [2, 0, 3, 1, 3, 2, 2, 3, 2, 2, 0, 1]
     h = N.hc_cache_create(c, labels, FAKE, N.hc_cache_bytes(c, labels))
@@ -245,6 +245,32 @@ def test_split_plan_for_benchmark_layers():
     lay = N.hc_cache_get_layout(h)
     assert (lay.global_splits, lay.sink_splits, lay.dummy_splits, lay.scratch_bytes) == (1, 1, 1, 0)
     N.hc_cache_destroy(h)
+
+
+def test_split_plan_models_the_dispatch():
+    """The split planner simulates the GPU's work-group dispatch (per XCD,
+    four queues of eight compute units, each in order).  On the benchmark
+    layers it picks the counts that measured fastest on MI355X among 1-8:
+    the 720p routed layer 3 Global splits (2 and 4 measured 38% and 10%
+    slower: their unit counts leave a third round in some queues), the
+    480p routed layer 3, the 480p and 1080p Global heads alone 4, and no
+    split for the 1080p routed layer, which fills the GPU by itself."""
+    def plan(name, labels):
+        from head_routed_kv_amd import workloads as W
+        wl = W.WORKLOADS[name]
+        c = N.make_config(len(labels), 128, wl.grid_h, wl.grid_w, 3, 21)
+        h = N.hc_cache_create(c, labels, FAKE, N.hc_cache_bytes(c, labels))
+        lay = N.hc_cache_get_layout(h)
+        N.hc_cache_destroy(h)
+        return lay.global_splits, lay.sink_splits, lay.dummy_splits
+    from head_routed_kv_amd import workloads as W
+    lab = {n: [int(x) for x in W.make_labels(W.WORKLOADS[n])] for n in ("480p", "720p", "1080p")}
+    assert plan("720p", lab["720p"])[0] == 3
+    assert plan("480p", lab["480p"])[0] == 3
+    assert plan("480p", [3] * lab["480p"].count(3))[0] == 4
+    assert plan("1080p", [3] * lab["1080p"].count(3))[0] == 4
+    assert plan("1080p", lab["1080p"]) == (1, 1, 1)
+    assert plan("720p", [3] * lab["720p"].count(3))[0] >= 5   # 5-8 measured within 0.5%
 
 
 def test_binding_checks_tensors_against_the_config():
