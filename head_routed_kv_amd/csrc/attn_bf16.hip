@@ -142,9 +142,11 @@ __device__ __forceinline__ void store_row4(void* base, int64_t off, f32x4 v) {
   }
 }
 
-template <int D, int QB, bool OUT_F32, bool GATHER, bool KV8 = false>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2 / QB, 2 / QB)))
-void attn_bf16_kernel(const AttnPlan P) {
+// One work unit: relative unit `rel` of category `ci` (ranged categories:
+// after the XCD run mapping).  Every thread of the work group calls it with
+// the same arguments and returns from it together.
+template <int D, int QB, bool OUT_F32, bool GATHER, bool KV8>
+__device__ __forceinline__ void attn_unit(const AttnPlan& P, const int ci, int rel, const int tid) {
   using TL = Tile<D>;
   constexpr int QT = 32 * QB * NW;   // queries per work group
   static_assert(!KV8 || (D == 128 && QB == 1 && !GATHER), "fp8 K/V: d = 128, ranged and cell-major kinds");
@@ -164,25 +166,7 @@ void attn_bf16_kernel(const AttnPlan P) {
   __shared__ int s_last;
   __shared__ float s_ml[NW][2][64];   // small units: each wave's (m, l) for the merge
 
-  const int u = blockIdx.x;
-  if (u >= P.total_units) return;
-  int ci = 0;
-#pragma unroll
-  for (int c = 1; c < 4; ++c)
-    if (c < P.n_cats && u >= P.cat[c].unit_begin) ci = c;
   const AttnCat& C = P.cat[ci];
-  int rel = u - C.unit_begin;
-  if (C.kind == KIND_RANGED) {
-    // Work groups reach the chip's eight XCDs round robin (block b on XCD
-    // b mod 8, each XCD taking its blocks in order), and each XCD has its own
-    // L2.  Hand every XCD a contiguous run of this category's units instead:
-    // the q tiles of one key range are consecutive units, so they then run on
-    // one or two XCDs and read the range through one or two L2s, not eight.
-    // Every XCD still gets the same number of units (to within one).
-    const int n = C.n_heads * C.units_per_head;
-    const int x = rel & 7, p = rel >> 3, q8 = n >> 3, r8 = n & 7;
-    rel = x * q8 + min(x, r8) + p;
-  }
   int slot, j;
   if (C.kind == KIND_RANGED || C.kind == KIND_BOX_GATHER) {
     slot = rel / C.units_per_head;
@@ -233,7 +217,6 @@ void attn_bf16_kernel(const AttnPlan P) {
     k0 = (C.kind == KIND_CELL_MAJOR) ? P.W * cell.off : 0;
   }
 
-  const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int l32 = lane & 31;
@@ -1061,6 +1044,84 @@ void attn_bf16_kernel(const AttnPlan P) {
   }
 }
 
+// Units of category ci on XCD x: ranged categories hand each XCD a contiguous
+// run of their units (the q tiles of one key range are consecutive, so a
+// range is read through one or two XCDs' L2s, not eight); the others every
+// eighth unit.  Every XCD gets the same number of units to within one.
+__device__ __forceinline__ int xcd_count(const AttnCat& C, int x) {
+  const int n = C.n_heads * C.units_per_head;
+  return C.kind == KIND_RANGED ? (n >> 3) + (x < (n & 7) ? 1 : 0) : (n > x ? (n - x + 7) >> 3 : 0);
+}
+__device__ __forceinline__ int xcd_unit(const AttnCat& C, int x, int i) {
+  const int n = C.n_heads * C.units_per_head;
+  return C.kind == KIND_RANGED ? x * (n >> 3) + min(x, n & 7) + i : x + 8 * i;
+}
+
+// Work groups reach the eight XCDs round robin (work group b on XCD b mod 8)
+// and each XCD has its own L2.
+//   Static mode (P.work_ctr == nullptr): one work group per unit; work group
+//   b of a category runs unit i of XCD b mod 8's run, i = its position there.
+//   Persistent mode: P.grid work groups; each takes the units of its XCD's
+//   list (categories in launch order, heaviest first) one after another,
+//   from a per-XCD counter, until the list is exhausted, so each XCD's
+//   compute units pick up work as they come free instead of in the fixed
+//   queue order of the hardware dispatcher.  The last work group of each XCD
+//   to finish resets its counters for the next launch.
+template <int D, int QB, bool OUT_F32, bool GATHER, bool KV8 = false>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2 / QB, 2 / QB)))
+void attn_bf16_kernel(const AttnPlan P) {
+  __shared__ int s_unit;
+  const bool persistent = P.work_ctr != nullptr;
+  const int x = blockIdx.x & 7;
+  // One copy of the unit body for both modes (static mode: one pass).
+  for (int pass = 0;; ++pass) {
+    int ci = -1, rel = 0;
+    if (!persistent) {
+      const int u = blockIdx.x;
+      if (pass > 0 || u >= P.total_units) break;
+      ci = 0;
+#pragma unroll
+      for (int c = 1; c < 4; ++c)
+        if (c < P.n_cats && u >= P.cat[c].unit_begin) ci = c;
+      rel = u - P.cat[ci].unit_begin;
+      if (P.cat[ci].kind == KIND_RANGED) rel = xcd_unit(P.cat[ci], rel & 7, rel >> 3);
+    } else {
+      if (threadIdx.x == 0)
+        s_unit = __hip_atomic_fetch_add(P.work_ctr + x, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+      int i = __builtin_amdgcn_readfirstlane(s_unit);
+      __syncthreads();   // s_unit is rewritten only after every thread has read it
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        if (c < P.n_cats && ci < 0) {
+          const int n = xcd_count(P.cat[c], x);
+          if (i < n) {
+            ci = c;
+            rel = xcd_unit(P.cat[c], x, i);
+          } else {
+            i -= n;
+          }
+        }
+      }
+      if (ci < 0) break;   // this XCD's list is exhausted (uniform over the work group)
+    }
+    // Opaque per pass: nothing the unit derives from the plan or the thread
+    // index is hoisted out of this loop and kept live across units (which
+    // would not fit the registers of two waves per SIMD).
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    attn_unit<D, QB, OUT_F32, GATHER, KV8>(P, ci, rel, tid);
+  }
+  if (!persistent) return;
+  if (threadIdx.x == 0) {
+    const int wgs = (P.grid - x + 7) >> 3;   // work groups of this XCD
+    if (__hip_atomic_fetch_add(P.work_ctr + 8 + x, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == wgs - 1) {
+      __hip_atomic_store(P.work_ctr + x, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(P.work_ctr + 8 + x, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_attn_bf16(const AttnPlan& plan, int head_dim, hipStream_t s) {
@@ -1070,7 +1131,7 @@ hipError_t launch_attn_bf16(const AttnPlan& plan, int head_dim, hipStream_t s) {
   const bool gather = gathers(plan.cat[0].kind);
   for (int c = 1; c < plan.n_cats; ++c)
     if (gathers(plan.cat[c].kind) != gather) return hipErrorInvalidValue;  // one mode per launch
-  dim3 grid(plan.total_units), block(NT);
+  dim3 grid(plan.work_ctr ? plan.grid : plan.total_units), block(NT);
 #define HC_LAUNCH(DD, F, G) hipLaunchKernelGGL((attn_bf16_kernel<DD, kBf16QueryBlocks, F, G>), grid, block, 0, s, plan)
   if (plan.kv8) {   // fp8 K/V: d = 128, bf16 output, cache kinds only
     if (head_dim != 128 || gather || f32) return hipErrorInvalidValue;

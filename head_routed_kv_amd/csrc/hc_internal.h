@@ -81,6 +81,12 @@ struct AttnPlan {
   // patches per frame down and across
   int32_t box_r, box_rows, box_cols_q, box_bands_y, box_bands_x;
   AttnCat cat[4];
+  // bf16 kernel, persistent mode: per-XCD unit counters [8] and finished-work-
+  // group counters [8], zero at launch and left zero; grid work groups.
+  // nullptr: one work group per unit.
+  int32_t* work_ctr;
+  int32_t grid;
+  int32_t pad2_;
   uint8_t head_of[4][HC_MAX_HEADS];  // category slot -> q/o head index
 };
 

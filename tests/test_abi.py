@@ -103,7 +103,8 @@ def test_fp8_cache_layout_halves_kv_bytes():
     N.hc_cache_destroy(h16)
     N.hc_cache_destroy(h8)
     # the 720p routed layer: the K/V region (everything before the split
-    # scratch) halves exactly; the fp32 scratch of the key splits does not
+    # scratch) halves exactly; the scratch (fp32 partials of the key splits,
+    # counters) follows each cache's own split plan
     c720 = dict(num_heads=12, head_dim=128, grid_h=45, grid_w=80, block_frames=3, window_frames=21)
     lab720 = [2, 0, 3, 1, 3, 2, 2, 3, 2, 2, 0, 1]
     lays = []
@@ -113,7 +114,7 @@ def test_fp8_cache_layout_halves_kv_bytes():
         lays.append(N.hc_cache_get_layout(h))
         N.hc_cache_destroy(h)
     assert lays[1].off_scratch * 2 == lays[0].off_scratch == 331_776_000
-    assert lays[1].scratch_bytes == lays[0].scratch_bytes
+    assert lays[0].scratch_bytes > 0 and lays[1].scratch_bytes > 0
 
 
 def test_cache_create_errors():
@@ -248,29 +249,30 @@ def test_split_plan_for_benchmark_layers():
 
 
 def test_split_plan_models_the_dispatch():
-    """The split planner simulates the GPU's work-group dispatch (per XCD,
-    four queues of eight compute units, each in order).  On the benchmark
-    layers it picks the counts that measured fastest on MI355X among 1-8:
-    the 720p routed layer 3 Global splits (2 and 4 measured 38% and 10%
-    slower: their unit counts leave a third round in some queues), the
-    480p routed layer 3, the 480p and 1080p Global heads alone 4, and no
-    split for the 1080p routed layer, which fills the GPU by itself."""
+    """The split planner simulates hc_attend's persistent launch (one work
+    group per compute unit, each XCD's 32 taking the units of its own list
+    as they come free) with unit costs measured on MI355X.  On the benchmark
+    layers it picks the counts that measured fastest there among 1-8 (or
+    within 1% of it): 4 Global splits for the 720p routed layer (2 measured
+    37% slower), 3 for the 480p routed layer, 4 for the 480p and 1080p
+    Global heads alone, 8 for the 720p Global heads alone, and no split for
+    the 1080p routed layer, which fills the GPU by itself."""
+    from head_routed_kv_amd import workloads as W
+
     def plan(name, labels):
-        from head_routed_kv_amd import workloads as W
         wl = W.WORKLOADS[name]
         c = N.make_config(len(labels), 128, wl.grid_h, wl.grid_w, 3, 21)
         h = N.hc_cache_create(c, labels, FAKE, N.hc_cache_bytes(c, labels))
         lay = N.hc_cache_get_layout(h)
         N.hc_cache_destroy(h)
         return lay.global_splits, lay.sink_splits, lay.dummy_splits
-    from head_routed_kv_amd import workloads as W
     lab = {n: [int(x) for x in W.make_labels(W.WORKLOADS[n])] for n in ("480p", "720p", "1080p")}
-    assert plan("720p", lab["720p"])[0] == 3
+    assert plan("720p", lab["720p"])[0] == 4
     assert plan("480p", lab["480p"])[0] == 3
     assert plan("480p", [3] * lab["480p"].count(3))[0] == 4
     assert plan("1080p", [3] * lab["1080p"].count(3))[0] == 4
+    assert plan("720p", [3] * lab["720p"].count(3))[0] == 8
     assert plan("1080p", lab["1080p"]) == (1, 1, 1)
-    assert plan("720p", [3] * lab["720p"].count(3))[0] >= 5   # 5-8 measured within 0.5%
 
 
 def test_binding_checks_tensors_against_the_config():
