@@ -203,13 +203,13 @@ def make_flush(device):
     return flush
 
 
-def layer_timing(layer, steps, flush):
+def layer_timing(layer, steps, flush, modes=("cold", "warm")):
     """HIP-event times of `steps` steady-state steps (append, then attend) of
     one layer: cold (each step preceded, untimed, by the 512 MiB write) and
     warm (back to back).  Returns per-step and per-attend samples in ms."""
     import torch
     res = {}
-    for mode in ("cold", "warm"):
+    for mode in modes:
         evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(steps)]
         torch.cuda.synchronize()
         for i in range(steps):
@@ -553,7 +553,7 @@ def main():
     ms_step = statistics.fmean(step_samples)
     attend_ms = statistics.fmean(attend_samples)
     # the same steps back to back (K/V partly served by the Infinity Cache)
-    warm = layer_timing(layer, a.steps, flush)["warm"]
+    warm = layer_timing(layer, a.steps, flush, modes=("warm",))["warm"]
     warm_step, warm_attend = statistics.fmean(warm["step"]), statistics.fmean(warm["attend"])
 
     work = algorithmic_work(wl, labels)

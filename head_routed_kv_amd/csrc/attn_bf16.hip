@@ -332,10 +332,9 @@ __device__ __forceinline__ void attn_unit(const AttnPlan& P, const int ci, int r
   };
   // fp8 K/V: lane p = 64*wave + lane moves 16-byte piece p of the K tile and
   // of the V tile (row p / (D/16), bytes 16*(p % (D/16)); one piece per
-  // thread at d = 128) from global memory into a row-major staging buffer,
-  // and later widens the same piece to bf16 in the ring buffer, at the
-  // swizzled slots the bf16 loads would have used.  E4M3 values are exact in
-  // bf16, so the rest of the kernel is unchanged.
+  // thread at d = 128) from global memory into a row-major staging buffer;
+  // `widen` later writes the tile to bf16 in the ring buffer, at the swizzled
+  // slots the bf16 loads would have used.
   const int p8 = 64 * wave + lane;
   const int r8 = p8 / (D / 16), c8 = p8 % (D / 16);
   const uint32_t ofs8 = (uint32_t)(min(r8, rows_avail - 1) * rowb + 16 * c8);
@@ -346,33 +345,34 @@ __device__ __forceinline__ void attn_unit(const AttnPlan& P, const int ci, int r
     lds_dma16(kt, ofs8, kd);
     lds_dma16(vt, ofs8, kd + KB8);
   };
+  // Widening: thread t writes bf16 chunks g = t and t + NT of the K tile and
+  // of the V tile (row g / 16, slot g % 16 at d = 128), converting the eight
+  // fp8 codes of the chunk the swizzle puts there.  Each 16 consecutive lanes
+  // thus write one whole 256-byte row, and each 8 one contiguous 128 bytes,
+  // the pattern LDS writes take without bank conflicts (a per-lane 32-byte
+  // piece written as two 16-byte slots is not).  E4M3 values are exact in
+  // bf16, so the rest of the kernel is unchanged.
   auto widen = [&](const uint8_t* stg, uint8_t* buf) {
 #pragma unroll
-    for (int kv = 0; kv < 2; ++kv) {
-      const u32x4 w = *(const u32x4*)(stg + kv * KB8 + 16 * p8);
-      bf16x8 h[2];
+    for (int kv = 0; kv < 2; ++kv)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {   // bytes 4i..4i+3 -> elements 4i..4i+3 of the piece
-        const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[i], 1.0f, false);
-        const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[i], 1.0f, true);
-        h[i >> 1][4 * (i & 1) + 0] = lo[0];
-        h[i >> 1][4 * (i & 1) + 1] = lo[1];
-        h[i >> 1][4 * (i & 1) + 2] = hi[0];
-        h[i >> 1][4 * (i & 1) + 3] = hi[1];
+      for (int q = 0; q < TL::KB / 16 / NT; ++q) {
+        const int g = q * NT + 64 * wave + lane;
+        const int row = g / TL::CPR, slot = g % TL::CPR;
+        const int chunk = slot ^ (kv == 0 ? swz_k<D>(row) : swz_v<D>(row));
+        const u32x2 w = *(const u32x2*)(stg + kv * KB8 + row * D + 8 * chunk);
+        bf16x8 h;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {   // bytes 4i..4i+3 -> elements 4i..4i+3 of the chunk
+          const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[i], 1.0f, false);
+          const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[i], 1.0f, true);
+          h[4 * i + 0] = lo[0];
+          h[4 * i + 1] = lo[1];
+          h[4 * i + 2] = hi[0];
+          h[4 * i + 3] = hi[1];
+        }
+        *(bf16x8*)(buf + kv * TL::KB + row * TL::ROWB + 16 * slot) = h;
       }
-      const int sw = kv == 0 ? swz_k<D>(r8) : swz_v<D>(r8);
-      uint8_t* row = buf + kv * TL::KB + r8 * TL::ROWB;
-      // The piece's two slots differ in bit 0.  Each write instruction stores,
-      // per lane, the half whose slot parity is its row's parity: the 8 lanes
-      // of an even row then fill the even slots of their row and the 8 lanes
-      // of the next (odd) row its odd slots, so every 16 consecutive lanes
-      // cover all banks once.  (Writing slot 2*c8 ^ sw first sends both rows
-      // to the even slots under the V swizzle, which keeps bit 0.)
-      const int s0 = (2 * c8) ^ sw, s1 = (2 * c8 + 1) ^ sw;
-      const bool swap = (s0 & 1) != (r8 & 1);
-      *(bf16x8*)(row + 16 * (swap ? s1 : s0)) = swap ? h[1] : h[0];
-      *(bf16x8*)(row + 16 * (swap ? s0 : s1)) = swap ? h[0] : h[1];
-    }
   };
 
   // ---- main loop -------------------------------------------------------------
