@@ -335,7 +335,8 @@ def rollout_costs(wl, labels, q, k, v, full_ms, steps_per_block=4, lengths=(14, 
     Warm-up: while the first window fills, every head attends over the growing
     window (each block: one push and steps_per_block - 1 replacements, an
     attend after each).  At first fill: hc_classify on the window, then the
-    window's blocks are replayed into the routed cache.  Afterwards each block's
+    window's blocks are replayed into the routed cache, whose memory is
+    allocated beforehand.  Afterwards each block's
     steps go through the routed cache.  The routed cache uses this layer's
     label mix (the classifier runs on the same random inputs only for its
     time).  Routed blocks are timed over 8 blocks; longer rollouts are
@@ -371,14 +372,15 @@ def rollout_costs(wl, labels, q, k, v, full_ms, steps_per_block=4, lengths=(14, 
                   for b in range(nb))
     kw, vw = sess.window_views()
     cls_ms = timed(lambda: hk.classify(cfg, q, kw, vw, workspace=ws))
-    holder = {}
+    # the routed cache's memory is allocated before the timed region, like the
+    # classifier workspace: restructuring is the window's block appends
+    routed = hk.RoutedCache(cfg, [int(x) for x in labels])
+    torch.cuda.synchronize()
 
     def restructure():
-        holder["c"] = hk.RoutedCache(cfg, [int(x) for x in labels])
         for b in range(nb):
-            holder["c"].append(*blk(kw, vw, b))
+            routed.append(*blk(kw, vw, b))
     rest_ms = timed(restructure)
-    routed = holder["c"]
     rep = lambda kb, vb: routed.append(kb, vb, hk.HC_REPLACE_NEWEST)
     n_timed = 8
     routed_ms = sum(timed(lambda b=b: block_steps(routed.append, rep, routed.attend, *blk(k, v, b % nb)))
