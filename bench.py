@@ -494,6 +494,9 @@ def main():
     ap.add_argument("--radius", type=int, default=2, help="sliding-box proxy radius")
     ap.add_argument("--kv", default="bf16", choices=("bf16", "fp8"),
                     help="K/V cache format of the timed layer (fp8: OCP E4M3 codes, bf16 arithmetic)")
+    ap.add_argument("--pathway", choices=("global", "sink", "dummy", "spatial"),
+                    help="profiling aid: time only this pathway's heads of the layer (no extras, no CPU leg); "
+                         "the line's roofline is then that pathway's (HBM for Spatial)")
     ap.add_argument("--calibrate", action="store_true",
                     help="also run a plain 1 GiB device copy (known bytes) to scale HBM counters")
     a = ap.parse_args()
@@ -505,6 +508,8 @@ def main():
     from head_routed_kv_amd import workloads as W
     wl = W.WORKLOADS[a.workload]
     labels = W.make_labels(wl, a.seed)
+    if a.pathway:
+        a.no_cpu = a.no_extra = True
     # the CPU leg first, before this process touches the GPU
     cpu = None if a.no_cpu else cpu_baseline(wl, labels, a.seed)
 
@@ -520,6 +525,16 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     q, k, v = gen_inputs(wl, a.seed, dev)
+    layer_name = f"{wl.name} routed layer"
+    if a.pathway:
+        lab = {"sink": 0, "dummy": 1, "spatial": 2, "global": 3}[a.pathway]
+        heads = [h for h in range(wl.heads) if int(labels[h]) == lab]
+        if not heads:
+            sys.exit(f"the {wl.name} layer has no {a.pathway} heads")
+        idx = torch.tensor(heads, device=dev)
+        q, k, v = q[idx].contiguous(), k[idx].contiguous(), v[idx].contiguous()
+        layer_name = f"{wl.name} {a.pathway} heads alone"
+        wl, labels = W.small(wl, heads=len(heads), name=wl.name), [lab] * len(heads)
     kvf = hk.HC_KV_FP8_E4M3 if a.kv == "fp8" else hk.HC_KV_SAME
     layer = Layer(wl, labels, q, k, v, kv_format=kvf)
     flush = make_flush(dev)
@@ -671,7 +686,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic N(0,1) bf16 Q/K/V (seeded), labels by the 25/40/20/15% Global/Spatial/Sink/Dummy mix",
-        "config": {"workload": f"{wl.name} routed layer", "heads": wl.heads, "head_dim": wl.head_dim,
+        "config": {"workload": layer_name, "heads": wl.heads, "head_dim": wl.head_dim,
                    "grid": [wl.grid_h, wl.grid_w], "block_frames": wl.block_frames,
                    "window_frames": wl.window_frames, "queries": wl.Nq, "keys": wl.Nk,
                    "labels": [int(x) for x in labels], "step": "append(REPLACE_NEWEST) + attend",
@@ -699,6 +714,12 @@ def main():
         "pathways": extra,
         "cpu_baseline": cpu,
     }
+    if a.pathway:
+        line["roofline"]["traffic"] = None   # the stored counter record is the routed layer's
+        if a.pathway == "spatial":           # an HBM-bound pathway: bytes against the HBM peak
+            gbs = alg_bytes / (attend_ms / 1e3) / 1e9
+            line["roofline"].update({"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)})
     print(json.dumps(line), flush=True)
 
 

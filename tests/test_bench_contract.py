@@ -74,3 +74,34 @@ def test_threshold_study_flop_fraction_matches_oracle_key_sets(name):
         want = sum(O.keyset_sizes(g, int(x)) for x in labels) / (wl.heads * O.keyset_sizes(g, O.GLOBAL))
         assert layer_flop_fraction(wl, labels) == pytest.approx(want, rel=1e-15)
     assert layer_flop_fraction(wl, [3] * wl.heads) == 1.0
+
+
+def test_threshold_table_from_the_oracles_diagnostics():
+    """The rule and threshold table of the graded planted workload, computed
+    from the oracle's stored diagnostics (the labels depend on the thresholds
+    only through the rule, not through the diagnostics): the oracle's rule at
+    every (theta, theta_sc), then the routed-FLOP fraction.  Rules 0 and 1
+    agree here, since no head clears two proxies."""
+    import json
+    from head_routed_kv_amd.threshold_study import layer_flop_fraction
+    from oracle import headcast_oracle as O
+    gold = json.load(open(os.path.join(ROOT, "tests", "golden", "classifier720p_graded_seed0.json")))
+    wl = W.WORKLOADS["classifier720p_graded"]
+    table = {   # theta: (fractions at theta_sc 0.6, 0.755, 0.9), label counts at 0.755 (Sink, Dummy, Spatial, Global)
+        0.85: ((0.557, 0.557, 0.606), (9, 6, 5, 20)),
+        0.90: ((0.600, 0.600, 0.648), (7, 6, 5, 22)),
+        0.95: ((0.624, 0.624, 0.648), (7, 6, 4, 23)),
+        0.98: ((0.648, 0.648, 0.648), (7, 6, 3, 24)),
+    }
+    for theta, (fracs, counts) in table.items():
+        for theta_sc, frac in zip((0.6, 0.755, 0.9), fracs):
+            labs = {}
+            for rule in (0, 1):
+                p = O.ClassifyParams(theta_sink=theta, theta_dummy=theta, theta_spatial=theta,
+                                     theta_score=theta_sc, rule=rule)
+                labs[rule] = [O.decide_label(d, p) for d in gold["diag"]]
+            assert labs[0] == labs[1]
+            assert round(layer_flop_fraction(wl, labs[0]), 3) == frac, (theta, theta_sc)
+            if theta_sc == 0.755:
+                assert tuple(labs[0].count(k) for k in range(4)) == counts
+    assert gold["planted"].count(0) == 9 and gold["planted"].count(1) == 6 and gold["planted"].count(2) == 12
