@@ -442,7 +442,7 @@ def counter_traffic(workload, kv="bf16"):
         return None
 
 
-def cpu_baseline(wl, labels, seed, rows_per_head=1024, procs=None):
+def cpu_baseline(wl, labels, seed, rows_per_head=2048, procs=None):
     """The oracle (fp64 numpy) on a bounded sample of the routed layer: every
     head, a seeded contiguous run of query rows, run process-parallel over
     (head, 512-row chunk) pieces with one BLAS thread per process.  Timed
@@ -463,7 +463,7 @@ def cpu_baseline(wl, labels, seed, rows_per_head=1024, procs=None):
     t0 = time.perf_counter()
     with ProcessPoolExecutor(min(procs, len(tasks)), mp_context=mp.get_context("spawn"),
                              initializer=pool._init_worker) as ex:
-        cpu_s = sum(sec for _, _, sec in ex.map(pool._run_task, [(wl, seed, h, lab, r0, n, 2)
+        cpu_s = sum(sec for _, _, sec in ex.map(pool._run_task, [(wl, seed, h, lab, r0, n, 2, None)
                                                                   for h, lab, r0, n in tasks], chunksize=2))
     el = time.perf_counter() - t0
     qh = rows_per_head * wl.heads

@@ -42,3 +42,19 @@ def test_chunks_cover_every_row_once():
         spans = sorted((t[4], t[5]) for t in tasks if t[2] == h)
         assert spans[0][0] == 0 and sum(n for _, n in spans) == wl.Nq
         assert all(a + n == b for (a, n), (b, _) in zip(spans, spans[1:]))
+
+
+def test_pool_fp8_cache_values():
+    """kv_scales: the workers attend over the oracle's E4M3 quantise-then-decode
+    of K and V, as an fp8 cache holds them."""
+    wl = W.small(W.WORKLOADS["720p"], grid_h=13, grid_w=22, heads=2, window_frames=6, name="pool-test")
+    ks, vs = 0.75, 1.5
+    res, _, _ = pool.run(wl, 4, [(0, O.GLOBAL), (1, O.SPATIAL)], rows_per_task=200, procs=2, kv_scales=(ks, vs))
+    g = O.Geometry(wl.grid_h, wl.grid_w, wl.block_frames, wl.window_frames, wl.cell_h, wl.cell_w)
+    for h, pw in ((0, O.GLOBAL), (1, O.SPATIAL)):
+        data = W.window(wl, seed=4, heads=[h], threads=1)
+        q, k, v = (W.as_float(data[n], wl)[0] for n in ("q", "k", "v"))
+        dk = O.dequantize_kv(O.quantize_kv(k, ks), ks)
+        dv = O.dequantize_kv(O.quantize_kv(v, vs), vs)
+        np.testing.assert_allclose(res[(h, pw)], O.attend_head(q, dk, dv, pw, g), rtol=0, atol=1e-12)
+        assert not np.allclose(dk, k)   # the codes do change the values
