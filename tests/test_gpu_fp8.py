@@ -7,6 +7,7 @@ import pytest
 import head_routed_kv_amd as hk
 from head_routed_kv_amd import workloads as W
 from oracle import headcast_oracle as O
+from oracle import pool
 from tests.gpu_util import BF16_TOL, check_close, geometry_of, sample_rows, say, to_float, torch, upload
 
 pytestmark = pytest.mark.gpu
@@ -113,6 +114,31 @@ def test_fp8_720p_pathway_alone_sampled(lab):
     rows = sample_rows(sub, 48, seed=lab)
     ref = oracle_fp8(sub, data, [lab] * len(heads), rows=rows)
     check_close(to_float(out)[:, rows], ref, BF16_TOL, f"fp8 pathway {lab} alone")
+
+
+@pytest.mark.timeout(900)   # the oracle side runs every row, process-parallel
+def test_fp8_720p_every_row():
+    """The 720p routed layer over an fp8 cache with scales that are not
+    powers of two, in the benchmark's launch configuration (its split plan
+    for fp8 caches): every query row of every head against the oracle on the
+    decoded K/V."""
+    wl = W.WORKLOADS["720p"]
+    labels = W.make_labels(wl)
+    say("case fp8 720p every row")
+    data = W.window(wl, seed=0)
+    q, k, v = (upload(data[n], wl) for n in ("q", "k", "v"))
+    cache = fill(wl, labels, k, v)
+    lay = cache.layout()
+    say("fp8 720p splits", lay.global_splits, lay.sink_splits, lay.dummy_splits)
+    out = cache.attend(q)
+    torch().cuda.synchronize()
+    got = to_float(out)
+    del q, k, v, out, cache
+    res, cpu_s, wall = pool.run(wl, 0, [(h, int(labels[h])) for h in range(wl.heads)], rows_per_task=1350,
+                                kv_scales=(K_SCALE, V_SCALE))
+    say(f"fp8 720p oracle: {cpu_s:.0f} s of CPU in {wall:.0f} s")
+    ref = np.stack([res[(h, int(labels[h]))] for h in range(wl.heads)])
+    check_close(got, ref, BF16_TOL, "fp8 720p every row")
 
 
 def test_fp8_720p_routed_sampled():
