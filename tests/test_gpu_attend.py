@@ -296,3 +296,30 @@ def test_max_heads_every_pathway():
     assert (lay.n_sink, lay.n_dummy, lay.n_spatial, lay.n_global) == (32, 32, 32, 32)
     assert [lay.head_slot[h] for h in range(128)] == [h // 4 for h in range(128)]
     check_close(to_float(out), oracle_routed(wl, data, labels), BF16_TOL, "128 heads")
+
+
+def test_two_caches_on_two_streams():
+    """Two 480p caches attend at the same time on two streams.  Each
+    persistent launch takes its units through its own cache's counters and
+    merges key splits through its own partials, so both outputs equal those of
+    the same calls made one after another, bit for bit, over three rounds."""
+    wl = W.WORKLOADS["480p"]
+    la = [int(x) for x in W.make_labels(wl)]
+    lb = [3 - x for x in la]
+    say("case two streams, labels", la, lb)
+    da, ca, ref_a = run_window(wl, la, seed=14)
+    db, cb, ref_b = run_window(wl, lb, seed=15)
+    assert ca.layout().global_splits > 1 or cb.layout().global_splits > 1
+    T = torch()
+    qa, qb = upload(da["q"], wl), upload(db["q"], wl)
+    sa, sb = T.cuda.Stream(), T.cuda.Stream()
+    for _ in range(3):
+        oa, ob = T.empty_like(qa), T.empty_like(qb)
+        T.cuda.synchronize()
+        with T.cuda.stream(sa):
+            ca.attend(qa, oa)
+        with T.cuda.stream(sb):
+            cb.attend(qb, ob)
+        T.cuda.synchronize()
+        assert np.array_equal(download_bits(oa), download_bits(ref_a))
+        assert np.array_equal(download_bits(ob), download_bits(ref_b))
