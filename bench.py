@@ -6,14 +6,16 @@ One step = one steady-state denoising step of one layer: the block being
 denoised gets new keys/values (hc_cache_append with REPLACE_NEWEST) and every
 head attends over its archetype's keys (hc_attend).  Inputs are synthetic
 N(0,1) bf16 of the workload's shape, resident in HBM before timing starts;
-the cache is restructured (W/B block appends) before timing.  The GPU's
-shader clock ramps up over the first ~100 ms of load, so untimed steps run
-for --clock-warmup seconds before the W warm-up steps.  The timed region is
-exactly K steps, each preceded (untimed) by a 512 MiB write, so that the
-layer's K/V come from HBM and not from the 256 MB Infinity Cache, as in a
-model step where the other layers' work evicts them; HIP events on the
-launch stream time each step and each hc_attend.  The same steps back to
-back are reported as "warm".
+the cache is restructured (W/B block appends) before timing.  The timed
+region is exactly K steps, each preceded (untimed) by a 512 MiB write, so
+that the layer's K/V come from HBM and not from the 256 MB Infinity Cache,
+as in a model step where the other layers' work evicts them; HIP events on
+the launch stream time each step and each hc_attend.  The same steps back to
+back are reported as "warm".  The GPU's clocks settle to each pattern of
+load over tens of milliseconds (ramping up at the start, and dipping for the
+first ~20 steps when write-then-attend steps follow back-to-back ones), so
+the untimed steps before each timed series run that series' own procedure:
+--clock-warmup seconds of them, then the W warm-up steps.
 
 Prints ONE JSON line with the metric, the roofline of the dominant kernel
 (the attention kernel), the same GPU's full-attention time (every head
@@ -203,15 +205,29 @@ def make_flush(device):
     return flush
 
 
-def layer_timing(layer, steps, flush, modes=("cold", "warm")):
+def settle(fn, flush=None, seconds=0.1):
+    """Untimed calls of fn (each preceded by flush(), if given) for `seconds`:
+    the procedure about to be timed, so the clocks have settled to it."""
+    import torch
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(5):
+            if flush is not None:
+                flush()
+            fn()
+        torch.cuda.synchronize()
+
+
+def layer_timing(layer, steps, flush, modes=("cold", "warm"), settle_s=0.1):
     """HIP-event times of `steps` steady-state steps (append, then attend) of
     one layer: cold (each step preceded, untimed, by the 512 MiB write) and
-    warm (back to back).  Returns per-step and per-attend samples in ms."""
+    warm (back to back), each series after settle_s seconds of its own
+    untimed steps.  Returns per-step and per-attend samples in ms."""
     import torch
     res = {}
     for mode in modes:
         evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(steps)]
-        torch.cuda.synchronize()
+        settle(layer.step, flush if mode == "cold" else None, settle_s)
         for i in range(steps):
             if mode == "cold":
                 flush()
@@ -238,8 +254,7 @@ def pathway_alone(wl, labels, work, q, k, v, flush, dev, iters):
         idx = torch.tensor(heads, device=dev)
         lay = Layer(W.small(wl, heads=len(heads)), [lab] * len(heads), q[idx].contiguous(), k[idx].contiguous(),
                     v[idx].contiguous())
-        for _ in range(2):
-            lay.attend()
+        settle(lay.attend, flush, 0.05)
         ms = time_events(lay.attend, iters, flush)
         f, by = work[lab]
         out[name] = {"heads": len(heads), "ms_cold": round(ms, 4),
@@ -259,14 +274,12 @@ def layer_line(wl, labels, seed, dev, flush, steps=10, alone=True):
     work = algorithmic_work(wl, labels)
     flops = sum(f for f, _ in work.values())
     lay = Layer(wl, labels, q, k, v)
-    for _ in range(3):
-        lay.step()
     t = layer_timing(lay, steps, flush)
     del lay
     full = Layer(wl, [3] * wl.heads, q, k, v)
-    for _ in range(2):
-        full.attend()
+    settle(full.attend, flush)
     full_cold = time_events(full.attend, 5, flush)
+    settle(full.attend)
     full_warm = time_events(full.attend, 5)
     del full
     torch.cuda.empty_cache()
@@ -540,12 +553,11 @@ def main():
     flush = make_flush(dev)
     torch.cuda.synchronize()
 
-    t_warm = time.perf_counter()
-    while time.perf_counter() - t_warm < a.clock_warmup:
-        for _ in range(10):
-            layer.step()
-        torch.cuda.synchronize()
+    # untimed: the timed procedure itself (write, append, attend) for
+    # --clock-warmup seconds, then the W warm-up steps
+    settle(layer.step, flush, a.clock_warmup)
     for _ in range(a.warmup):
+        flush()
         layer.step()
     torch.cuda.synchronize()
     # Timed region: exactly K steps, each preceded (untimed) by a 512 MiB write,
@@ -584,9 +596,9 @@ def main():
 
     # full-attention baseline on the same GPU: every head Global, same inputs
     full = Layer(wl, [3] * wl.heads, q, k, v, kv_format=kvf)
-    for _ in range(3):
-        full.attend()
+    settle(full.attend, flush)
     full_cold_ms = time_events(full.attend, 10, flush)
+    settle(full.attend)
     full_ms = time_events(full.attend, 10)
     full_flops = wl.heads * 4 * wl.head_dim * wl.Nq * wl.Nk
     full_splits = full.cache.layout().global_splits
@@ -599,8 +611,6 @@ def main():
         # the same layer over an fp8 (E4M3) K/V cache: K/V bytes halve, the
         # attention arithmetic stays bf16
         l8 = Layer(wl, labels, q, k, v, kv_format=hk.HC_KV_FP8_E4M3)
-        for _ in range(3):
-            l8.step()
         t8 = layer_timing(l8, 10, flush)
         ms8, ms8_cold = statistics.fmean(t8["warm"]["attend"]), statistics.fmean(t8["cold"]["attend"])
         step8 = statistics.fmean(t8["cold"]["step"])
@@ -617,8 +627,7 @@ def main():
             sub = W.small(wl, heads=len(sp))
             ls8 = Layer(sub, [2] * len(sp), q[idx].contiguous(), k[idx].contiguous(), v[idx].contiguous(),
                         kv_format=hk.HC_KV_FP8_E4M3)
-            for _ in range(3):
-                ls8.attend()
+            settle(ls8.attend, flush, 0.05)
             ms = time_events(ls8.attend, 10, flush)
             f, by = work[2]
             by8 = by - (by - 2 * 2 * sub.heads * sub.Nq * sub.head_dim) // 2   # K/V read once at 1 byte
