@@ -987,22 +987,35 @@ __device__ __forceinline__ void attn_unit(const AttnPlan& P, const int ci, int r
 #pragma unroll
     for (int b = 0; b < QB; ++b) {
       if (!qvalid[b]) continue;
+      // (m, l) of every split: all loads issued before any result is used
+      // (addresses past the last split repeat its own), then the maximum.
       float ms[kMaxSplits], ls[kMaxSplits];
+#pragma unroll
+      for (int s = 0; s < kMaxSplits; ++s)
+        load_coherent(pml0 + (int64_t)min(s, splits - 1) * QT + qlocal[b], ms[s], ls[s]);
       float M = -INFINITY;
 #pragma unroll
-      for (int s = 0; s < kMaxSplits; ++s) {   // splits <= kMaxSplits; all loads issued together
-        load_coherent(pml0 + (int64_t)min(s, splits - 1) * QT + qlocal[b], ms[s], ls[s]);
+      for (int s = 0; s < kMaxSplits; ++s)
         if (s < splits) M = fmaxf(M, ms[s]);
-      }
       float L = 0.f;
       float acc[D / 2];   // this lane's 16 (D=128) or 8 (D=64) column quadruples
 #pragma unroll
       for (int i = 0; i < D / 2; ++i) acc[i] = 0.f;
+      // Splits in index order whichever merges, so the sum is the same in
+      // every run; this split's own partial is still in its registers
+      // (acc[16t + j] pairs with oacc[b][t][j]).
 #pragma unroll
       for (int s = 0; s < kMaxSplits; ++s) {
         if (s >= splits) break;   // uniform
         const float w = __builtin_amdgcn_exp2f((ms[s] - M) * c2);
         L = fmaf(w, ls[s], L);
+        if (s == split) {   // uniform
+#pragma unroll
+          for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) acc[16 * t + j] = fmaf(w, oacc[b][t][j], acc[16 * t + j]);
+          continue;
+        }
         const uint64_t* ps = (const uint64_t*)(C.part + ((int64_t)id * splits + s) * QT * D);
         float x[D / 2];
 #pragma unroll
