@@ -1002,14 +1002,15 @@ __device__ __forceinline__ void attn_unit(const AttnPlan& P, const int ci, int r
 #pragma unroll
       for (int i = 0; i < D / 2; ++i) acc[i] = 0.f;
       // Splits in index order whichever merges, so the sum is the same in
-      // every run; this split's own partial is still in its registers
-      // (acc[16t + j] pairs with oacc[b][t][j]).
+      // every run.  With a bf16 output this split's own partial is taken
+      // from its registers (acc[16t + j] pairs with oacc[b][t][j]); the fp32
+      // output variants read it back, which keeps them within the registers.
 #pragma unroll
       for (int s = 0; s < kMaxSplits; ++s) {
         if (s >= splits) break;   // uniform
         const float w = __builtin_amdgcn_exp2f((ms[s] - M) * c2);
         L = fmaf(w, ls[s], L);
-        if (s == split) {   // uniform
+        if (!OUT_F32 && s == split) {   // uniform
 #pragma unroll
           for (int t = 0; t < D / 32; ++t)
 #pragma unroll
