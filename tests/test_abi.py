@@ -292,3 +292,36 @@ def test_binding_checks_tensors_against_the_config():
         hk.check_tensor(ok, c, 96, "q_block")
     with pytest.raises(ValueError, match="contiguous channels"):
         hk.tensor_arg(torch.zeros(4, 64, 96, dtype=torch.bfloat16).transpose(1, 2))
+
+
+def test_c_program_against_the_header_and_library(tmp_path):
+    """tests/c/abi_host.c, compiled as C11 with gcc against include/headcast.h
+    and linked to libheadcast.so, runs the host-only entry points and agrees
+    with the Python binding."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    libdir = os.path.dirname(N.LIB_PATH)
+    exe = tmp_path / "abi_host"
+    cmd = [gcc, "-std=c11", "-Wall", "-Werror", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+           "-I", os.path.join(rocm, "include"), os.path.join(ROOT, "tests", "c", "abi_host.c"), "-o", str(exe),
+           "-L", libdir, "-l:" + os.path.basename(N.LIB_PATH), "-Wl,-rpath," + libdir]
+    subprocess.run(cmd, check=True, capture_output=True, text=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True, timeout=60).stdout
+    got = dict(line.split(" ", 1) for line in out.strip().splitlines())
+    labels = [2, 0, 3, 1, 3, 2, 2, 3, 2, 2, 0, 1]
+    c = N.make_config(12, 128, 45, 80, 3, 21)
+    assert int(got["validate"]) == 0 and int(got["create"]) == 0 and int(got["destroy"]) == 0
+    assert int(got["cache_bytes"]) == N.hc_cache_bytes(c, labels)
+    h = N.hc_cache_create(c, labels, FAKE, N.hc_cache_bytes(c, labels))
+    lay = N.hc_cache_get_layout(h)
+    N.hc_cache_destroy(h)
+    assert (int(got["n_global"]), int(got["n_spatial"]), int(got["n_sink"]), int(got["n_dummy"])) == (3, 5, 2, 2)
+    assert int(got["global_splits"]) == lay.global_splits
+    assert int(got["workspace"]) == N.hc_classify_workspace_bytes(c)
+    assert float(got["theta_score"]) == pytest.approx(0.755) and float(got["gamma"]) == pytest.approx(5.0)
+    code, name = got["bad"].split()
+    assert int(code) != 0 and name.startswith("HC_ERR") and got["message_nonempty"] == "1"
