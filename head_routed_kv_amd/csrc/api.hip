@@ -64,7 +64,6 @@ hc_status check_config(const hc_config* c) {
     return fail(HC_ERR_INVALID_ARG, "kv_format %d is not HC_KV_SAME or HC_KV_FP8_E4M3", c->kv_format);
   if (kv_fp8(c)) {
     if (c->dtype != HC_BF16) return fail(HC_ERR_DTYPE, "fp8 K/V need dtype HC_BF16");
-    if (c->head_dim != 128) return fail(HC_ERR_UNSUPPORTED, "fp8 K/V are implemented for head_dim 128 only");
     for (float sc : {c->k_scale, c->v_scale})
       if (!(sc >= 0.f) || !std::isfinite(sc)) return fail(HC_ERR_INVALID_ARG, "k_scale and v_scale must be finite and >= 0");
   }

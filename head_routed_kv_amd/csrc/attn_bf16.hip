@@ -149,7 +149,7 @@ template <int D, int QB, bool OUT_F32, bool GATHER, bool KV8>
 __device__ __forceinline__ void attn_unit(const AttnPlan& P, const int ci, int rel, const int tid) {
   using TL = Tile<D>;
   constexpr int QT = 32 * QB * NW;   // queries per work group
-  static_assert(!KV8 || (D == 128 && QB == 1 && !GATHER), "fp8 K/V: d = 128, ranged and cell-major kinds");
+  static_assert(!KV8 || (QB == 1 && !GATHER), "fp8 K/V: ranged and cell-major kinds");
   // The bf16 ring buffers (K tile then V tile each): four, tile j in buffer
   // j mod 4; with fp8 K/V three, tile j in buffer j mod 3, fed from a ring of
   // three fp8 staging buffers.  Separate objects rather than one indexed
@@ -338,12 +338,16 @@ __device__ __forceinline__ void attn_unit(const AttnPlan& P, const int ci, int r
   const int p8 = 64 * wave + lane;
   const int r8 = p8 / (D / 16), c8 = p8 % (D / 16);
   const uint32_t ofs8 = (uint32_t)(min(r8, rows_avail - 1) * rowb + 16 * c8);
+  // A staged fp8 tile is KB8 / 1 KiB direct loads for K and as many for V:
+  // one each for every wave at d = 128, for waves 0-3 at d = 64.
   auto load8 = [&](int lb, uint8_t* stg) {
-    const char* kt = Kc + (int64_t)(k0 + lb) * rowb;   // uniform tile base
-    const char* vt = Vc + (int64_t)(k0 + lb) * rowb;
-    const uint32_t kd = lds_addr(stg) + 1024 * wave;
-    lds_dma16(kt, ofs8, kd);
-    lds_dma16(vt, ofs8, kd + KB8);
+    if (wave < KB8 / 1024) {   // wave-uniform
+      const char* kt = Kc + (int64_t)(k0 + lb) * rowb;   // uniform tile base
+      const char* vt = Vc + (int64_t)(k0 + lb) * rowb;
+      const uint32_t kd = lds_addr(stg) + 1024 * wave;
+      lds_dma16(kt, ofs8, kd);
+      lds_dma16(vt, ofs8, kd + KB8);
+    }
   };
   // Widening: thread t writes bf16 chunks g = t and t + NT of the K tile and
   // of the V tile (row g / 16, slot g % 16 at d = 128), converting the eight
@@ -1147,9 +1151,14 @@ hipError_t launch_attn_bf16(const AttnPlan& plan, int head_dim, hipStream_t s) {
     if (gathers(plan.cat[c].kind) != gather) return hipErrorInvalidValue;  // one mode per launch
   dim3 grid(plan.work_ctr ? plan.grid : plan.total_units), block(NT);
 #define HC_LAUNCH(DD, F, G) hipLaunchKernelGGL((attn_bf16_kernel<DD, kBf16QueryBlocks, F, G>), grid, block, 0, s, plan)
-  if (plan.kv8) {   // fp8 K/V: d = 128, bf16 output, cache kinds only
-    if (head_dim != 128 || gather || f32) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((attn_bf16_kernel<128, kBf16QueryBlocks, false, false, true>), grid, block, 0, s, plan);
+  if (plan.kv8) {   // fp8 K/V: bf16 output, cache kinds only
+    if (gather || f32) return hipErrorInvalidValue;
+    if (head_dim == 128)
+      hipLaunchKernelGGL((attn_bf16_kernel<128, kBf16QueryBlocks, false, false, true>), grid, block, 0, s, plan);
+    else if (head_dim == 64)
+      hipLaunchKernelGGL((attn_bf16_kernel<64, kBf16QueryBlocks, false, false, true>), grid, block, 0, s, plan);
+    else
+      return hipErrorInvalidValue;
   } else if (head_dim == 128) {
     if (gather) { if (f32) HC_LAUNCH(128, true, true); else HC_LAUNCH(128, false, true); }
     else { if (f32) HC_LAUNCH(128, true, false); else HC_LAUNCH(128, false, false); }

@@ -57,7 +57,6 @@ def test_status_strings():
     (dict(softmax_scale=-1.0), N.HC_ERR_INVALID_ARG),
     (dict(kv_format=2), N.HC_ERR_INVALID_ARG),
     (dict(kv_format=N.HC_KV_FP8_E4M3, dtype=N.HC_FP32), N.HC_ERR_DTYPE),
-    (dict(kv_format=N.HC_KV_FP8_E4M3, head_dim=64), N.HC_ERR_UNSUPPORTED),
     (dict(kv_format=N.HC_KV_FP8_E4M3, k_scale=-1.0), N.HC_ERR_INVALID_ARG),
     (dict(kv_format=N.HC_KV_FP8_E4M3, v_scale=float("inf")), N.HC_ERR_INVALID_ARG),
 ])

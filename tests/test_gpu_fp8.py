@@ -44,11 +44,12 @@ def oracle_fp8(wl, data, labels, rows=None, heads=None, k_scale=K_SCALE, v_scale
     return np.stack([O.attend_head(fq[h], dk[h], dv[h], int(labels[h]), g, rows=rows) for h in heads])
 
 
-def test_fp8_cache_codes_bit_exact():
+@pytest.mark.parametrize("d", [128, 64])
+def test_fp8_cache_codes_bit_exact(d):
     """Every archetype buffer holds the oracle's E4M3 codes of the blocks, in
     the documented layout, through a ring wrap and a replacement; one block
     is scaled up so that codes saturate at +-448."""
-    wl = W.Workload("bits8", 19, 6, 128, 13, 23, 2, 6, "bf16", "uniform")
+    wl = W.Workload("bits8", 19, 6, d, 13, 23, 2, 6, "bf16", "uniform")
     labels = [2, 3, 0, 1, 3, 2]
     g = geometry_of(wl)
     cache = hk.RoutedCache(fp8_config(wl), labels)
@@ -79,12 +80,13 @@ def test_fp8_cache_codes_bit_exact():
     assert saturated > 0
 
 
-def test_fp8_attend_every_pathway_small():
+@pytest.mark.parametrize("d", [128, 64])
+def test_fp8_attend_every_pathway_small(d):
     """Several q tiles and key tiles with ragged tails, uneven border cells,
     all four pathways; repeat calls are bit-identical."""
-    wl = W.Workload("small8", 20, 8, 128, 23, 37, 2, 6, "bf16", "uniform")
+    wl = W.Workload("small8", 20, 8, d, 23, 37, 2, 6, "bf16", "uniform")
     labels = [0, 1, 2, 3, 3, 2, 1, 0]
-    say("case fp8 small")
+    say("case fp8 small, d", d)
     data = W.window(wl, seed=5)
     q, k, v = (upload(data[n], wl) for n in ("q", "k", "v"))
     cache = fill(wl, labels, k, v)
