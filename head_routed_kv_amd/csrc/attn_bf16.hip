@@ -341,7 +341,7 @@ __device__ __forceinline__ void attn_unit(const AttnPlan& P, const int ci, int r
   // A staged fp8 tile is KB8 / 1 KiB direct loads for K and as many for V:
   // one each for every wave at d = 128, for waves 0-3 at d = 64.
   auto load8 = [&](int lb, uint8_t* stg) {
-    if (wave < KB8 / 1024) {   // wave-uniform
+    if (KB8 >= 1024 * NW || wave < KB8 / 1024) {   // wave-uniform; always true at d = 128
       const char* kt = Kc + (int64_t)(k0 + lb) * rowb;   // uniform tile base
       const char* vt = Vc + (int64_t)(k0 + lb) * rowb;
       const uint32_t kd = lds_addr(stg) + 1024 * wave;
