@@ -323,3 +323,27 @@ def test_two_caches_on_two_streams():
         T.cuda.synchronize()
         assert np.array_equal(download_bits(oa), download_bits(ref_a))
         assert np.array_equal(download_bits(ob), download_bits(ref_b))
+
+
+def test_split_merges_repeat_bit_for_bit_under_load():
+    """The three 720p Global heads alone: the planner splits each key range 8
+    ways, so one launch has 1,032 units and 129 merges, each reading partials
+    that other XCDs wrote with device-coherent stores.  Twenty launches back
+    to back give the same bits; a merge that read a stale or partly written
+    partial would not.  The first launch is also held to the oracle on
+    sampled rows."""
+    wl720 = W.WORKLOADS["720p"]
+    heads = [h for h in range(wl720.heads) if int(W.make_labels(wl720)[h]) == O.GLOBAL]
+    wl = W.small(wl720, heads=len(heads))
+    say("case 720p Global heads alone, 20 launches")
+    data, cache, out = run_window(wl, [O.GLOBAL] * len(heads), seed=21)
+    assert cache.layout().global_splits == 8
+    first = download_bits(out)
+    q = upload(data["q"], wl)
+    outs = [cache.attend(q) for _ in range(20)]
+    torch().cuda.synchronize()
+    for i, o in enumerate(outs):
+        assert np.array_equal(download_bits(o), first), i
+    rows = sample_rows(wl, 24, seed=3)
+    check_close(to_float(out)[:, rows], oracle_routed(wl, data, [O.GLOBAL] * len(heads), rows=rows), BF16_TOL,
+                "720p Global alone, 8 splits")
