@@ -230,6 +230,25 @@ def test_1080p_every_head_sampled_rows():
     check_close(got, ref, BF16_TOL, "1080p sampled rows, all heads")
 
 
+@pytest.mark.timeout(900)   # the oracle side runs every row of four heads, process-parallel
+def test_1080p_every_row_one_head_per_pathway():
+    """The 1080p layer (40 heads) in its benchmark launch: every query row of
+    the first head of each pathway (171,360 keys per Global query, the
+    8-row border cells for Spatial) against the oracle."""
+    wl = W.WORKLOADS["1080p"]
+    labels = W.make_labels(wl)
+    heads = [next(h for h in range(wl.heads) if int(labels[h]) == lab)
+             for lab in (O.GLOBAL, O.SINK, O.DUMMY, O.SPATIAL)]
+    say("case 1080p every row, heads", heads)
+    data, cache, out = run_window(wl, labels)
+    got = to_float(out[heads])
+    del data, cache, out
+    res, cpu_s, wall = pool.run(wl, 0, [(h, int(labels[h])) for h in heads], rows_per_task=1224)
+    say(f"1080p oracle: {cpu_s:.0f} s of CPU in {wall:.0f} s")
+    ref = np.stack([res[(h, int(labels[h]))] for h in heads])
+    check_close(got, ref, BF16_TOL, "1080p every row, one head per pathway")
+
+
 @pytest.mark.parametrize("lab", [O.GLOBAL, O.SINK, O.DUMMY, O.SPATIAL])
 def test_720p_pathway_alone_sampled(lab):
     """Each pathway's heads of the 720p layer alone, as the benchmark's
