@@ -303,6 +303,60 @@ def layer_line(wl, labels, seed, dev, flush, steps=10, alone=True):
     return res
 
 
+def head_costs(wl):
+    """Planned cost of one head per pathway label: its algorithmic flops at
+    the matrix peak or its algorithmic bytes at the HBM peak, whichever takes
+    longer (seconds)."""
+    out = {}
+    for lab in range(4):
+        f, by = algorithmic_work(wl, [lab])[lab]
+        out[lab] = max(f / (PEAK_BF16_TFLOPS * 1e12), by / (PEAK_HBM_GBS * 1e9))
+    return out
+
+
+def shard_heads(labels, cost, n_gpus):
+    """Heads onto n_gpus by longest-processing-time packing: heads by
+    decreasing cost (ties: lower head first), each onto the GPU with the
+    least planned cost so far (ties: lower GPU first).  Returns the sorted
+    head list of each GPU."""
+    order = sorted(range(len(labels)), key=lambda h: (-cost[int(labels[h])], h))
+    load = [0.0] * n_gpus
+    shards = [[] for _ in range(n_gpus)]
+    for h in order:
+        g = min(range(n_gpus), key=lambda i: (load[i], i))
+        shards[g].append(h)
+        load[g] += cost[int(labels[h])]
+    return [sorted(s) for s in shards]
+
+
+def gpu_shares(wl, labels, seed, dev, flush, n_gpus=8, iters=5):
+    """One GPU's share of the layer when its heads are sharded over n_gpus
+    GPUs (attention needs no exchange between them): each share's heads as
+    a cache of their own, timed cold on this GPU.  The layer's time on
+    n_gpus GPUs is the slowest share's."""
+    import torch
+    from head_routed_kv_amd import workloads as W
+    q, k, v = gen_inputs(wl, seed, dev)
+    shares = []
+    for heads in shard_heads(labels, head_costs(wl), n_gpus):
+        if not heads:
+            shares.append({"heads": [], "labels": [], "ms_cold": 0.0})
+            continue
+        idx = torch.tensor(heads, device=dev)
+        labs = [int(labels[h]) for h in heads]
+        lay = Layer(W.small(wl, heads=len(heads)), labs, q[idx].contiguous(), k[idx].contiguous(),
+                    v[idx].contiguous())
+        settle(lay.attend, flush, 0.05)
+        shares.append({"heads": heads, "labels": labs, "ms_cold": round(time_events(lay.attend, iters, flush), 4)})
+        del lay, idx
+    del q, k, v
+    torch.cuda.empty_cache()
+    slowest = max(s["ms_cold"] for s in shares)
+    return {"n_gpus": n_gpus, "shares": shares, "layer_ms": slowest,
+            "query_heads_per_s": round(wl.heads * wl.Nq / (slowest / 1e3)),
+            "balance": round(sum(s["ms_cold"] for s in shares) / n_gpus / slowest, 4)}
+
+
 def launch_overhead(wl, labels, seed, dev, n_layers=30, reps=5):
     """A denoising step of an n_layers-deep model as far as this layer type
     goes: for each layer, append (REPLACE_NEWEST) then attend, each layer
@@ -641,6 +695,9 @@ def main():
         for name, seed_off in (("480p", 3), ("1080p", 1)):
             wx = W.WORKLOADS[name]
             extra[name] = layer_line(wx, W.make_labels(wx, a.seed), a.seed + seed_off, dev, flush)
+        # one GPU's share of the 1080p layer with its 40 heads sharded over 8 GPUs
+        w10 = W.WORKLOADS["1080p"]
+        extra["1080p"]["sharded"] = gpu_shares(w10, W.make_labels(w10, a.seed), a.seed + 1, dev, flush)
         # launch overhead of a 30-layer step, eager against one HIP-graph replay
         extra["launch_overhead"] = {name: launch_overhead(W.WORKLOADS[name], W.make_labels(W.WORKLOADS[name], a.seed),
                                                           a.seed, dev)

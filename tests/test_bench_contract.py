@@ -105,3 +105,36 @@ def test_threshold_table_from_the_oracles_diagnostics():
             if theta_sc == 0.755:
                 assert tuple(labs[0].count(k) for k in range(4)) == counts
     assert gold["planted"].count(0) == 9 and gold["planted"].count(1) == 6 and gold["planted"].count(2) == 12
+
+
+def test_1080p_head_shards_over_8_gpus():
+    """Longest-processing-time packing of the 1080p layer's 40 heads onto 8
+    GPUs.  Every head lands on exactly one GPU.  With 10 Global heads on 8
+    GPUs some GPU must hold two of them (pigeonhole), so no plan can do
+    better than twice a Global head's cost; this one reaches that bound,
+    and no GPU is left idle."""
+    wl = W.WORKLOADS["1080p"]
+    labels = W.make_labels(wl)
+    counts = {lab: int(sum(1 for x in labels if int(x) == lab)) for lab in range(4)}
+    assert counts == {3: 10, 2: 16, 0: 8, 1: 6}
+    cost = bench.head_costs(wl)
+    # Global and Sink/Dummy heads are priced by their flops, Spatial heads by their bytes
+    assert cost[3] == bench.algorithmic_work(wl, [3])[3][0] / (bench.PEAK_BF16_TFLOPS * 1e12)
+    assert cost[0] == cost[1] < cost[3]
+    assert cost[2] == bench.algorithmic_work(wl, [2])[2][1] / (bench.PEAK_HBM_GBS * 1e9)
+    shards = bench.shard_heads(labels, cost, 8)
+    assert sorted(h for s in shards for h in s) == list(range(40))
+    loads = [sum(cost[int(labels[h])] for h in s) for s in shards]
+    assert max(loads) == pytest.approx(2 * cost[3])
+    assert all(s for s in shards)
+    assert sum(loads) / 8 < max(loads)
+
+
+def test_head_shards_small_cases():
+    cost = {0: 1.0, 1: 1.0, 2: 0.5, 3: 4.0}
+    # one GPU takes everything, in head order
+    assert bench.shard_heads([3, 0, 2], cost, 1) == [[0, 1, 2]]
+    # heaviest first, each to the least-loaded GPU, ties to the lower GPU
+    assert bench.shard_heads([0, 3, 1, 3], cost, 2) == [[0, 1], [2, 3]]
+    # more GPUs than heads: the extra GPUs stay empty
+    assert bench.shard_heads([2, 2], cost, 3) == [[0], [1], []]
