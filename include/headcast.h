@@ -100,8 +100,8 @@ enum { HC_PUSH_BLOCK = 0, HC_REPLACE_NEWEST = 1 };
  *                                   KV bytes are the cost the restructure
  *                                   cuts).  Needs dtype HC_BF16 (else
  *                                   HC_ERR_DTYPE); head_dim 64 or 128.
- *                                   hc_cache_append
- *                                   still takes bf16 blocks and stores
+ *                                   hc_cache_append still takes bf16
+ *                                   blocks and stores
  *                                   code(fp32(x * fp32(1/scale))), rounded to
  *                                   nearest even and saturated at +-448
  *                                   (inputs must be finite); hc_attend runs
